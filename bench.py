@@ -1,0 +1,255 @@
+"""Benchmark of the attention forward pass (libfa355) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one call of fa_fwd (one kernel launch) over one batch of seeded
+synthetic inputs already resident in HBM.  The default workload is the
+LLM-prefill shape B=4 H=32 N=4096 d=128, bf16, causal.  Prints ONE JSON line
+on stdout (human-readable detail goes to stderr):
+
+  value      attention TFLOP/s = 4 B H N^2 d (halved for causal) / time per step
+  roofline   the kernel against the bf16 dense matrix-core peak, with its
+             average launch duration measured by HIP events on the launch
+             stream, and (when a counter summary of the current kernel source
+             is committed under profiles/) its HBM traffic per launch
+  cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
+             of the same workload (whole heads), scaled to TFLOP/s
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import fa_inputs  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak, B4 H32 N4096 d128 causal, 1 GPU"
+# MI355X dense bf16 matrix-core peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["flashattention_forward_07_amd/csrc/fa_fwd_kernel.hip",
+                  "flashattention_forward_07_amd/csrc/fa_fwd_launch.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_flops(lengths, H, d, causal):
+    """4 N^2 d per head (Q K^T and P V, 2 flops per multiply-add), halved when
+    causal -- the metric's convention."""
+    n2 = float(np.sum(np.asarray(lengths, dtype=np.float64) ** 2))
+    f = 4.0 * H * n2 * d
+    return f / 2.0 if causal else f
+
+
+def algorithmic_bytes(total_tokens, H, d, elem):
+    """Compulsory HBM bytes: read Q, K, V once, write O once, write lse."""
+    return total_tokens * H * (4 * d * elem + 4)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload_name):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload_name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the oracle on whole heads of the workload until ~budget_s."""
+    import oracle
+    # the host share of this GPU: OMP_NUM_THREADS when set, else the affinity mask
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    if w.varlen:
+        cu = inp.cu_seqlens
+        order = np.argsort(np.diff(cu))[::-1]  # long sequences first
+        for s in order:
+            a, b = int(cu[s]), int(cu[s + 1])
+            for h in range(w.H):
+                oracle.attention(inp.q[a:b, h], inp.k[a:b, h], inp.v[a:b, h], w.scale, w.causal)
+                flops += attention_flops([b - a], 1, w.d, w.causal)
+                heads += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = f"{heads} whole (sequence, head) slices, longest sequences first"
+    else:
+        B, H = w.B, w.H
+        for i in range(B * H):
+            b, h = divmod(i, H)
+            oracle.attention(inp.q[b, h], inp.k[b, h], inp.v[b, h], w.scale, w.causal)
+            flops += attention_flops([w.N], 1, w.d, w.causal)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        sample = f"{heads} of {B * H} whole (batch, head) slices"
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample}; {flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=fa_inputs.HEADLINE.name,
+                    choices=[w.name for w in fa_inputs.WORKLOADS])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain 1 GiB device copy (for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (every (batch, head) is independent, so several GPUs would each run "
+              "this kernel on their own heads).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import flashattention_forward_07_amd as fa
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+
+    w = fa_inputs.by_name(args.workload)
+    log(f"[bench] workload {w.name}: generating seeded inputs")
+    inp = fa_inputs.make(w)
+    elem = 2 if w.dtype == "bf16" else 4
+    code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+
+    def dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(x).to("cuda")
+
+    q, k, v = (dev(x) for x in inp.device_arrays())
+    o = torch.empty_like(q)
+    if w.varlen:
+        T = inp.q.shape[0]
+        lse = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+        cu = torch.from_numpy(inp.cu_seqlens).to("cuda")
+        lengths = np.diff(inp.cu_seqlens)
+        nseq = lengths.size
+
+        def step():
+            fa.fa_fwd_varlen(q, k, v, o, lse, cu, nseq, w.max_len, w.H, w.d, w.scale, w.causal,
+                             code)
+        total_tokens = int(inp.cu_seqlens[-1])
+    else:
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        lengths = [w.N] * w.B
+
+        def step():
+            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, code)
+        total_tokens = w.B * w.N
+
+    flops = attention_flops(lengths, w.H, w.d, w.causal)
+    alg_bytes = algorithmic_bytes(total_tokens, w.H, w.d, elem)
+
+    stream = torch.cuda.current_stream()  # fa_fwd launches on this stream
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_ms = float(np.mean(per_launch_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"[bench] kernel mean {kern_ms:.4f} ms, median {np.median(per_launch_ms):.4f} ms, "
+        f"min {np.min(per_launch_ms):.4f} ms; wall {ms_per_step:.4f} ms/step")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    traffic = committed_traffic(w.name)
+    log(f"[bench] {value:.1f} TFLOP/s per step, kernel {achieved:.1f} TFLOP/s = "
+        f"{100 * achieved / peak:.1f}% of {peak:.1f}; algorithmic bytes {alg_bytes / 1e6:.1f} MB "
+        f"-> {alg_bytes / (kern_ms * 1e-3) / 1e9:.0f} GB/s")
+
+    result = {
+        "metric": METRIC if w is fa_inputs.HEADLINE else f"attention fwd TFLOP/s, {w.name}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B if not w.varlen else int(len(lengths)),
+                   "H": w.H, "N": w.N if not w.varlen else int(max(lengths)), "d": w.d,
+                   "causal": w.causal, "varlen": w.varlen, "tokens": total_tokens,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle on the host (~{args.cpu_budget:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+        log(f"[bench] cpu baseline {result['cpu_baseline']}")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+// fa355_api.hip -- the C ABI declared in include/fa355.h: host-side argument
+// validation, stride set-up and dispatch to the forward kernels.  Every
+// check runs before anything is enqueued; on error nothing is launched.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "fa355.h"
+#include "fa_fwd_launch.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+constexpr long long kMaxRows = 1ll << 40;  // B*H*N bound keeps every offset in int64
+constexpr long long kMaxGrid = 0x7fffffffll;
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Checks that do not depend on the problem being non-empty.
+int value_checks(int d, float scale, int dtype) {
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+// Pointer checks, for non-empty problems (an empty one may pass NULLs).
+int pointer_checks(const void *q, const void *k, const void *v, void *o, const float *lse) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+      misaligned(lse, 4))
+    return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int launch(const fa355::FwdArgs &a, int dtype, int d, int causal, bool varlen, void *stream) {
+  const hipError_t e =
+      fa355::launch_fwd(a, dtype, d, causal != 0, varlen, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                  int N, int d, float scale, int causal, int dtype, void *stream) {
+  int st = value_checks(d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  st = pointer_checks(q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  const long long bh = (long long)B * H;  // < 2^62, no overflow
+  const long long n_qtiles = (N + fa355::kBlockM - 1) / fa355::kBlockM;
+  if (bh > kMaxRows / N || bh > kMaxGrid / n_qtiles) return FA_ERR_SHAPE;
+  const long long rows = bh * N;
+
+  const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  const size_t tbytes = (size_t)rows * d * esz;
+  if (overlap(o, tbytes, q, tbytes) || overlap(o, tbytes, k, tbytes) ||
+      overlap(o, tbytes, v, tbytes))
+    return FA_ERR_ALIAS;
+  if (lse) {
+    const size_t lbytes = (size_t)rows * sizeof(float);
+    if (overlap(lse, lbytes, q, tbytes) || overlap(lse, lbytes, k, tbytes) ||
+        overlap(lse, lbytes, v, tbytes) || overlap(lse, lbytes, o, tbytes))
+      return FA_ERR_ALIAS;
+  }
+
+  fa355::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_seqlens = nullptr;
+  a.row_stride = d;
+  a.head_stride = (long long)N * d;
+  a.seq_stride = (long long)H * N * d;
+  a.lse_row_stride = 1;
+  a.lse_head_stride = N;
+  a.lse_seq_stride = (long long)H * N;
+  a.n = N;
+  a.H = H;
+  a.n_qtiles = (int)n_qtiles;
+  a.grid = (int)(bh * n_qtiles);
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  return launch(a, dtype, d, causal, false, stream);
+}
+
+FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                         const int *cu_seqlens, int nseq, int max_seqlen, int H, int d,
+                         float scale, int causal, int dtype, void *stream) {
+  int st = value_checks(d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (nseq < 0 || H < 0 || max_seqlen < 0) return FA_ERR_SHAPE;
+  if (nseq == 0 || H == 0 || max_seqlen == 0) return FA_OK;
+  st = pointer_checks(q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  if (!cu_seqlens) return FA_ERR_NULL;
+  if (misaligned(cu_seqlens, 4)) return FA_ERR_ALIGN;
+  const long long n_qtiles = (max_seqlen + fa355::kBlockM - 1) / fa355::kBlockM;
+  if ((long long)nseq * H > kMaxGrid / n_qtiles) return FA_ERR_SHAPE;
+  if (o == q || o == k || o == v || (lse && (void *)lse == o)) return FA_ERR_ALIAS;
+
+  fa355::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_seqlens = cu_seqlens;
+  a.row_stride = (long long)H * d;
+  a.head_stride = d;
+  a.seq_stride = 0;
+  a.lse_row_stride = H;
+  a.lse_head_stride = 1;
+  a.lse_seq_stride = 0;
+  a.n = 0;
+  a.H = H;
+  a.n_qtiles = (int)n_qtiles;
+  a.grid = (int)((long long)nseq * H * n_qtiles);
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  return launch(a, dtype, d, causal, true, stream);
+}
+
+FA_API const char *fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or oversized problem size";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors need 16-byte alignment, lse 4-byte";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
+    case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed (see fa_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+FA_API int fa_last_hip_error(void) { return g_last_hip; }
+
+FA_API const char *fa_version(void) { return "libfa355 0.1.0 gfx950"; }
+
+}  // extern "C"

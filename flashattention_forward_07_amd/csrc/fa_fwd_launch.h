@@ -1,0 +1,45 @@
+// fa_fwd_launch.h -- internal interface between the C ABI (fa355_api.hip)
+// and the forward kernels (fa_fwd_kernel.hip).  Not installed, not part of
+// the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa355 {
+
+// Everything a forward launch needs.  Element strides address one
+// (sequence, head) slice: token i of sequence s, head h starts at
+//   seq_base(s) + h * head_stride + i * row_stride
+// where seq_base(s) = s * seq_stride for a fixed-length batch and
+// cu_seqlens[s] * row_stride for a packed one.  lse uses the same scheme
+// with its own strides.
+struct FwdArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  void *o;
+  float *lse;             // may be null
+  const int *cu_seqlens;  // device, packed batches only
+  long long seq_stride;
+  long long head_stride;
+  long long row_stride;
+  long long lse_seq_stride;
+  long long lse_head_stride;
+  long long lse_row_stride;
+  int n;         // sequence length (fixed-length batches)
+  int H;         // heads
+  int n_qtiles;  // query tiles per (sequence, head)
+  int grid;      // workgroups launched
+  float scale;       // softmax scale applied to q.k
+  float scale_log2;  // scale * log2(e), for exp2
+};
+
+// Query rows per workgroup.
+constexpr int kBlockM = 128;
+
+// Enqueue the forward kernel for (dtype, d, causal, varlen).  Returns the
+// HIP status of the launch.
+hipError_t launch_fwd(const FwdArgs &a, int dtype, int d, bool causal,
+                      bool varlen, hipStream_t stream);
+
+}  // namespace fa355

@@ -1,0 +1,120 @@
+/*
+ * fa355.h -- C ABI of libfa355, an exact attention forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (page "Mini FlashAttention", section 1 "What attention
+ * is"; the same definition opens "How Did I Write My First FlashAttention
+ * Kernel in CUDA?"): for every (batch, head) with rows q_i, k_j, v_j,
+ *     S = Q K^T * scale,   P = softmax(S) along each row,   O = P V,
+ * with the optional causal mask S[i][j] = -inf for j > i.  The library
+ * computes it as the pages' flash algorithm does -- a resident block of
+ * query rows, K/V tiles streamed past it, a running row max m, denominator
+ * l and output accumulator rescaled by exp(m_old - m_new) per tile, and one
+ * division O / l at the end ("Mini FlashAttention", section 4; the grasp.study
+ * lesson, "The Complete Kernel: Initialization, Loop, and Finalization") --
+ * so the N x N score matrix never reaches memory.  It also returns, per row,
+ *     lse_i = ln sum_{j allowed} exp(S[i][j])      (natural log, fp32),
+ * the log of the softmax denominator, which lets partial results over
+ * disjoint key ranges be merged exactly.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing, frees nothing, keeps no workspace and
+ *     never synchronises.
+ *   - A call validates its arguments on the host; on any error it returns a
+ *     nonzero FA_ERR_* code and enqueues nothing.  On success it enqueues
+ *     one kernel on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and returns FA_OK at once.  Faults inside the kernel surface
+ *     at the caller's next synchronisation, as usual for HIP.
+ *   - q, k, v and o share one element type, `dtype`: FA_DTYPE_BF16
+ *     (bfloat16 storage; products and sums in fp32, the softmax weights
+ *     rounded to bf16 for the P.V product, output rounded to nearest even)
+ *     or FA_DTYPE_F32 (fp32 throughout).  lse is always fp32.
+ *   - Head dimension d is 64 or 128.  q, k, v and o must be 16-byte
+ *     aligned, lse 4-byte aligned; o and lse must not overlap q, k, v or
+ *     each other.
+ *   - `scale` must be finite and > 0 (the pages use 1/sqrt(d)).
+ *   - The error state is per host thread (fa_last_hip_error), so calls from
+ *     several threads are safe.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_API __attribute__((visibility("default")))
+
+/* element types */
+#define FA_DTYPE_F32 0
+#define FA_DTYPE_BF16 1
+
+/* status codes */
+#define FA_OK 0
+#define FA_ERR_NULL 1     /* a required pointer is NULL */
+#define FA_ERR_SHAPE 2    /* negative size, or a size too large to index */
+#define FA_ERR_HEAD_DIM 3 /* d is not 64 or 128 */
+#define FA_ERR_DTYPE 4    /* dtype is not FA_DTYPE_F32 / FA_DTYPE_BF16 */
+#define FA_ERR_SCALE 5    /* scale is not finite and > 0 */
+#define FA_ERR_ALIGN 6    /* a tensor pointer is misaligned */
+#define FA_ERR_ALIAS 7    /* an output overlaps an input or the other output */
+#define FA_ERR_HIP 8      /* the HIP launch failed; see fa_last_hip_error() */
+
+/*
+ * fa_fwd -- attention forward over a fixed-length batch.
+ *
+ *   q, k, v  [B, H, N, d] contiguous, dtype elements (read only)
+ *   o        [B, H, N, d] contiguous, dtype elements (written)
+ *   lse      [B, H, N] fp32 (written), or NULL to skip it
+ *   causal   0: every query sees all N keys; nonzero: query i sees keys
+ *            0..i (the causal mask of "Mini FlashAttention", section 1)
+ *
+ * Each (b, h) slice is the pages' row-major [N, d] matrix.  B, H or N equal
+ * to 0 is an empty problem: FA_OK, nothing enqueued, pointers not examined
+ * (they may be NULL).  Validation order: dtype, d, scale, sizes, then
+ * pointers (NULL, alignment, overlap).
+ */
+FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o,
+                  float *lse, int B, int H, int N, int d, float scale,
+                  int causal, int dtype, void *stream);
+
+/*
+ * fa_fwd_varlen -- attention forward over a packed batch of sequences of
+ * different lengths (the pages speak of ragged sequences; the packing is
+ * this library's).
+ *
+ *   q, k, v     [T, H, d] contiguous (token-major), T = cu_seqlens[nseq]
+ *   o           [T, H, d] contiguous (written)
+ *   lse         [T, H] fp32 (written), or NULL
+ *   cu_seqlens  DEVICE int32 [nseq + 1]: sequence s owns tokens
+ *               cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends only to
+ *               them; the causal mask uses positions local to the sequence.
+ *   max_seqlen  host int >= every sequence length (it sizes the grid)
+ *
+ * Preconditions the host cannot check without reading device memory, so
+ * the caller guarantees them: cu_seqlens[0] == 0, non-decreasing, and no
+ * length above max_seqlen (rows past max_seqlen would be left unwritten).
+ * o must not overlap q, k, v or lse (only exact pointer equality is
+ * detected here, since T is not known on the host).  nseq, H or max_seqlen
+ * equal to 0 is an empty problem, as for fa_fwd.
+ */
+FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o,
+                         float *lse, const int *cu_seqlens, int nseq,
+                         int max_seqlen, int H, int d, float scale,
+                         int causal, int dtype, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+FA_API const char *fa_status_string(int status);
+
+/* The hipError_t of this thread's last FA_ERR_HIP (0 if none). */
+FA_API int fa_last_hip_error(void);
+
+/* Library version string, e.g. "libfa355 0.1.0 gfx950". */
+FA_API const char *fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

@@ -1,0 +1,132 @@
+"""The C ABI library: it loads, exports every symbol include/fa355.h declares,
+and rejects bad arguments on the host before anything is enqueued.  No call
+here reaches the GPU (every call fails validation or is an empty problem)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import flashattention_forward_07_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+F32, BF16 = 0, 1
+A = 0x10000  # a 16-byte aligned fake address; never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"FA_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)
+
+
+def _status_codes():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define (FA_(?:OK|ERR_\w+)) (\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        pytest.skip("libfa355.so not built")
+    return fa.load()
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared()) == {"fa_fwd", "fa_fwd_varlen", "fa_status_string",
+                                "fa_last_hip_error", "fa_version"}
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else with the public prefix leaks out
+    assert {n for n in exported if n.startswith("fa_")} == set(_declared())
+
+
+def test_version_and_status_strings(lib):
+    assert fa.fa_version().startswith("libfa355")
+    assert "gfx950" in fa.fa_version()
+    codes = _status_codes()
+    assert codes["FA_OK"] == 0
+    for name, code in codes.items():
+        assert fa.fa_status_string(code).startswith(name)
+    assert fa.fa_status_string(12345) == "unknown status"
+    assert fa.fa_last_hip_error() == 0
+
+
+def _fwd(lib, q=A, k=A + 0x1000, v=A + 0x2000, o=A + 0x3000, lse=None, B=1, H=1, N=16,
+         d=64, scale=0.125, causal=0, dtype=BF16):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), causal, dtype, None)
+
+
+def _fwd_varlen(lib, q=A, k=A + 0x1000, v=A + 0x2000, o=A + 0x3000, lse=None, cu=A + 0x4000,
+                nseq=2, max_seqlen=16, H=1, d=64, scale=0.125, causal=0, dtype=BF16):
+    return lib.fa_fwd_varlen(q, k, v, o, lse, cu, nseq, max_seqlen, H, d, ctypes.c_float(scale),
+                             causal, dtype, None)
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    c = _status_codes()
+    assert _fwd(lib, q=None) == c["FA_ERR_NULL"]
+    assert _fwd(lib, o=None) == c["FA_ERR_NULL"]
+    assert _fwd(lib, dtype=2) == c["FA_ERR_DTYPE"]
+    assert _fwd(lib, dtype=-1) == c["FA_ERR_DTYPE"]
+    for d in (0, 32, 96, 256):
+        assert _fwd(lib, d=d) == c["FA_ERR_HEAD_DIM"]
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert _fwd(lib, scale=s) == c["FA_ERR_SCALE"]
+    assert _fwd(lib, q=A + 8) == c["FA_ERR_ALIGN"]
+    assert _fwd(lib, o=A + 0x3002) == c["FA_ERR_ALIGN"]
+    assert _fwd(lib, lse=A + 0x5002) == c["FA_ERR_ALIGN"]
+    assert _fwd(lib, B=-1) == c["FA_ERR_SHAPE"]
+    assert _fwd(lib, H=-2) == c["FA_ERR_SHAPE"]
+    assert _fwd(lib, N=-3) == c["FA_ERR_SHAPE"]
+    assert _fwd(lib, B=1 << 30, H=1 << 30, N=1 << 30) == c["FA_ERR_SHAPE"]
+    # o overlapping an input, lse overlapping o
+    assert _fwd(lib, o=A) == c["FA_ERR_ALIAS"]
+    assert _fwd(lib, o=A + 0x2000 + 1024) == c["FA_ERR_ALIAS"]
+    assert _fwd(lib, lse=A + 0x3000 + 64) == c["FA_ERR_ALIAS"]
+
+
+def test_fwd_empty_problem_is_a_no_op(lib):
+    for kw in ({"B": 0}, {"H": 0}, {"N": 0}):
+        assert _fwd(lib, **kw) == 0
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    c = _status_codes()
+    assert _fwd_varlen(lib, cu=None) == c["FA_ERR_NULL"]
+    assert _fwd_varlen(lib, cu=A + 0x4002) == c["FA_ERR_ALIGN"]
+    assert _fwd_varlen(lib, nseq=-1) == c["FA_ERR_SHAPE"]
+    assert _fwd_varlen(lib, max_seqlen=-1) == c["FA_ERR_SHAPE"]
+    assert _fwd_varlen(lib, d=80) == c["FA_ERR_HEAD_DIM"]
+    assert _fwd_varlen(lib, dtype=7) == c["FA_ERR_DTYPE"]
+    assert _fwd_varlen(lib, o=A) == c["FA_ERR_ALIAS"]
+    assert _fwd_varlen(lib, nseq=1 << 20, max_seqlen=1 << 30, H=64) == c["FA_ERR_SHAPE"]
+    assert _fwd_varlen(lib, nseq=0) == 0
+    assert _fwd_varlen(lib, max_seqlen=0) == 0
+
+
+def test_python_binding_raises_on_error(lib):
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd(A, A + 0x1000, A + 0x2000, A + 0x3000, None, 1, 1, 16, 96, 0.1, False, BF16,
+                  stream=0)
+    assert e.value.status == _status_codes()["FA_ERR_HEAD_DIM"]
+
+
+def test_product_package_does_not_reach_the_oracle():
+    # The product path never imports, links or loads the oracle.
+    pkg = os.path.dirname(fa.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("no fallback", ""), f
+                assert "fa_ref" not in text, f
