@@ -38,6 +38,7 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_forward_07_amd/csrc/fa_fwd_kernel.hip",
+                  "flashattention_forward_07_amd/csrc/fa_common.h",
                   "flashattention_forward_07_amd/csrc/fa_fwd_launch.h"]
 
 

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa355.so")
-SOURCES = ["fa355_api.hip", "fa_fwd_kernel.hip"]
+SOURCES = ["fa355_api.hip", "fa_fwd_kernel.hip", "fa_fwd_f32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are switched off for all device code.
@@ -21,7 +21,7 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang"
 
 
 def command(out: str = LIB, extra=()) -> list:
-    return ([HIPCC, *DEVICE_FLAGS, "-O3", "-std=c++17", "-fPIC", "-shared",
+    return ([HIPCC, *DEVICE_FLAGS, "-O3", "-std=c++20", "-fPIC", "-shared",
              "-fvisibility=hidden", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
             + [os.path.join(CSRC, s) for s in SOURCES] + list(extra) + ["-o", out])
 

@@ -66,7 +66,7 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *l
   st = pointer_checks(q, k, v, o, lse);
   if (st != FA_OK) return st;
   const long long bh = (long long)B * H;  // < 2^62, no overflow
-  const long long n_qtiles = (N + fa355::kBlockM - 1) / fa355::kBlockM;
+  const long long n_qtiles = (N + fa355::kMinBlockM - 1) / fa355::kMinBlockM;
   if (bh > kMaxRows / N || bh > kMaxGrid / n_qtiles) return FA_ERR_SHAPE;
   const long long rows = bh * N;
 
@@ -96,9 +96,9 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *l
   a.lse_head_stride = N;
   a.lse_seq_stride = (long long)H * N;
   a.n = N;
+  a.batch = B;
   a.H = H;
-  a.n_qtiles = (int)n_qtiles;
-  a.grid = (int)(bh * n_qtiles);
+  a.max_len = N;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   return launch(a, dtype, d, causal, false, stream);
@@ -115,7 +115,7 @@ FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, f
   if (st != FA_OK) return st;
   if (!cu_seqlens) return FA_ERR_NULL;
   if (misaligned(cu_seqlens, 4)) return FA_ERR_ALIGN;
-  const long long n_qtiles = (max_seqlen + fa355::kBlockM - 1) / fa355::kBlockM;
+  const long long n_qtiles = (max_seqlen + fa355::kMinBlockM - 1) / fa355::kMinBlockM;
   if ((long long)nseq * H > kMaxGrid / n_qtiles) return FA_ERR_SHAPE;
   if (o == q || o == k || o == v || (lse && (void *)lse == o)) return FA_ERR_ALIAS;
 
@@ -133,9 +133,9 @@ FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, f
   a.lse_head_stride = 1;
   a.lse_seq_stride = 0;
   a.n = 0;
+  a.batch = nseq;
   a.H = H;
-  a.n_qtiles = (int)n_qtiles;
-  a.grid = (int)((long long)nseq * H * n_qtiles);
+  a.max_len = max_seqlen;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
   return launch(a, dtype, d, causal, true, stream);

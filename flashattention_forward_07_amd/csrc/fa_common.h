@@ -1,0 +1,77 @@
+// fa_common.h -- device helpers shared by the forward kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_fwd_launch.h"
+
+namespace fa355 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+#define FA_GLOBAL __attribute__((address_space(1)))
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// Row (key) of a 32 x 32 matrix-core output block held in accumulator
+// register r by a lane of half h = lane / 32.
+__device__ __forceinline__ int block_key(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Hardware workgroup id -> logical id such that each XCD receives one
+// contiguous logical range (a bijection on [0, grid)).
+__device__ __forceinline__ int xcd_remap(int i, int grid) {
+  const int q = grid / kXcds, r = grid % kXcds;
+  const int x = i % kXcds, k = i / kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// Where a workgroup's query tile lives.
+struct TileCoords {
+  int n;            // length of its sequence
+  int m0;           // first query row of the tile
+  long long base;   // element offset of (sequence, head) token 0
+  long long lbase;  // lse offset of (sequence, head) token 0
+};
+
+// Logical workgroup -> (sequence, head, query tile); query tiles of one head
+// are issued heaviest (last rows) first.
+template <bool VARLEN>
+__device__ __forceinline__ TileCoords tile_coords(const FwdArgs &a, int block_m) {
+  const int L = xcd_remap(blockIdx.x, a.grid);
+  const int bh = L / a.n_qtiles;
+  const int qt = a.n_qtiles - 1 - (L - bh * a.n_qtiles);
+  const int s = bh / a.H;
+  const int hd = bh - s * a.H;
+  TileCoords c;
+  if constexpr (VARLEN) {
+    const int t0 = a.cu_seqlens[s];
+    c.n = a.cu_seqlens[s + 1] - t0;
+    c.base = (long long)t0 * a.row_stride;
+    c.lbase = (long long)t0 * a.lse_row_stride;
+  } else {
+    c.n = a.n;
+    c.base = (long long)s * a.seq_stride;
+    c.lbase = (long long)s * a.lse_seq_stride;
+  }
+  c.base += (long long)hd * a.head_stride;
+  c.lbase += (long long)hd * a.lse_head_stride;
+  c.m0 = qt * block_m;
+  return c;
+}
+
+}  // namespace fa355

@@ -1,472 +1,459 @@
-// fa_fwd_kernel.hip -- attention forward kernels for gfx950 (MI355X, CDNA4).
+// fa_fwd_kernel.hip -- attention forward for bf16 inputs on gfx950 (MI355X).
 //
-// One workgroup owns a block of kBlockM = 128 query rows of one (sequence,
-// head): four wave64s, each with 32 rows held in registers for the whole
-// kernel.  K/V tiles of BN keys stream through double-buffered LDS; for
-// every tile a wave computes its 32 x BN scores on the matrix cores, runs
-// the online-softmax update on them in registers, and adds P.V into an fp32
-// accumulator on the matrix cores.  This is the resident-query loop order
-// of "Mini FlashAttention", section 4 (and the initialise / loop / finalise
-// structure of the grasp.study lesson "The Complete Kernel: Initialization,
-// Loop, and Finalization"): state m = -inf, l = 0, O = 0; per tile
-//     m_new = max(m, rowmax S),  alpha = exp(m - m_new),
-//     P = exp(S - m_new),  l = alpha l + rowsum P,  O = alpha O + P V;
-// and O / l once at the end.  The score matrix never leaves registers.
+// The method is the resident-query flash loop of "Mini FlashAttention",
+// section 4 (with the initialise / loop / finalise structure of the
+// grasp.study lesson "The Complete Kernel: Initialization, Loop, and
+// Finalization"): per query row a running max m, denominator l and fp32
+// output accumulator O; each K/V tile of 64 keys gives scores S, the state is
+// rescaled by exp(m_old - m_new), P = exp(S - m) is added into l and P.V into
+// O, and O / l is formed once at the end.  Scores and P never leave
+// registers.
 //
-// Matrix-core layout (gfx950 v_mfma_f32_32x32x16_bf16, D = A.B + C with
-// A 32x16, B 16x32): the kernel computes the TRANSPOSED score block
-// S^T = K . Q^T, so that the 32 output columns are the wave's 32 queries.
-// An output lane l then holds query (l % 32) and 16 keys of a 32-key block,
-// keys 8*(r/4) + 4*(l/32) + r%4 for accumulator register r.  Row max and row
-// sum are therefore 15 in-register operations plus one exchange with lane
-// l ^ 32, and the per-row rescale factor is a per-lane scalar.  The same
-// registers, rounded to bf16, are the B operand of O^T += V^T . P^T once the
-// contraction index is re-labelled: in the 16-key chunk c the operand's
-// k = 8*(l/32) + e is taken to be key 16c + 8*(e/4) + 4*(l/32) + e%4, which
-// is exactly what lane l already holds.  V is therefore stored TRANSPOSED in
-// LDS ([d][key]) with bits 2 and 3 of the key position swapped, so every
-// A operand of the P.V product is one 16-byte LDS read.
+// Workgroup: 8 wave64s, 256 query rows, 32 per wave, held in registers as
+// the B operand of the matrix-core products.  The waves form two groups of
+// four (waves 0-3 and 4-7); a CU runs one workgroup, so every SIMD hosts one
+// wave of each group.  The groups run the same loop half a step apart and
+// alternate between two phases separated by workgroup barriers:
+//   M(t): S_t = K_t . Q^T  and  O^T += V_{t-1}^T . P_{t-1}^T   (matrix cores)
+//   V(t): mask S_t, row max, P_t = exp2(...), l, rescale O       (VALU)
+// so while one wave of a SIMD issues matrix-core work the other issues the
+// softmax, and the two overlap.
 //
-// fp32 inputs use v_mfma_f32_32x32x2_f32 with the same output layout (one
-// element per lane per operand, so K and V stay row-major in LDS and P stays
-// fp32); only the operand plumbing differs, the tile loop, masking,
-// softmax and finalisation are shared.
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16, D = A.B + C, A 32x16, B
+// 16x32; lane l holds A[l%32][8(l/32)..+7], B[8(l/32)..+7][l%32] and output
+// rows 8(r/4) + 4(l/32) + r%4 of column l%32 in register r).  The kernel
+// forms the TRANSPOSED score block S^T = K . Q^T: output column = query, so
+// a lane owns one query and 16 keys of each 32-key block; the row max is 15
+// in-register maxima plus one v_permlane32_swap with lane l ^ 32, and the
+// rescale factor is a per-lane scalar.  Those registers, rounded to bf16,
+// are the B operand of O^T += V^T . P^T after relabelling the contraction
+// index: in 16-key chunk c, operand index 8(l/32) + e stands for key
+// 16c + 8(e/4) + 4(l/32) + e%4, which is what lane l holds.
+//
+// LDS: K and V tiles stay row-major ([key][d], as in memory) in a 4-stage
+// ring filled by direct global->LDS loads (global_load_lds_dwordx4) issued
+// two tiles ahead, so no registers stage them.  Operands are read with
+// 64-bit LDS reads: K as two ds_read_b64 per 16-byte operand, V^T with
+// ds_read_b64_tr_b16, which hands each lane one d column of four key rows
+// (lanes 4e..4e+3 of a 16-lane group address row e, lane i receives element
+// i of each row).  16-byte chunks are XOR-swizzled per row so that every
+// read is free of bank conflicts: K chunk j of row r sits at slot j ^ sk(r),
+// V chunk j at j ^ sv(r).
+//
+// Lazy rescaling: the exponent reference m is raised only when a tile's row
+// max exceeds it by more than 8 / (scale log2 e), i.e. when a weight would
+// exceed 2^8; otherwise the old reference is kept and the rescale factor is
+// exactly 1.  The result is unchanged in exact arithmetic (any reference
+// cancels in O / l) and the weights stay <= 256, far from fp32 overflow.
 //
 // Masking: keys at or past the sequence end score -inf (the pages fill
 // padded key rows with zeros, which would give them score 0; the definition
-// sums over real keys only), and in causal mode key j > query i scores -inf
-// ("Mini FlashAttention", section 1).  Tiles entirely above a wave's
-// diagonal are skipped.  The running max is replaced by 0 whenever it is
-// still -inf before it is used as the exponent shift, the ghost-row guard of
-// "Mini FlashAttention", section 4, so no row can produce NaN; query rows
-// past the sequence end compute on zeros and are never stored.
-//
-// Work order: workgroups are dispatched round-robin over the 8 XCDs of the
-// chip (hardware id i runs on XCD i % 8).  The id is remapped so that each
-// XCD receives a contiguous range of logical tiles, i.e. all query tiles of
-// a (sequence, head) share one XCD and its L2, which then serves their
-// repeated K/V reads.  Within a head, causal tiles are issued heaviest
-// (last rows, most keys) first.
+// sums over real keys only), in causal mode key j > query i scores -inf
+// ("Mini FlashAttention", section 1), tiles entirely above a wave's diagonal
+// are skipped, and a -inf reference is replaced by 0 before use, the
+// ghost-row guard of "Mini FlashAttention", section 4.  Query rows past the
+// sequence end compute on zeros and are never stored.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
+#include "fa_common.h"
 #include "fa_fwd_launch.h"
 
 namespace fa355 {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kWaves = 8;
+constexpr int kThreads = kWave * kWaves;  // 512
+constexpr int kBlockM = 32 * kWaves;      // 256 query rows
+constexpr int kBN = 64;                   // keys per tile
+constexpr int kStages = 4;
 
-constexpr int kWave = 64;
-constexpr int kWaves = kBlockM / 32;
-constexpr int kThreads = kWave * kWaves;
-constexpr int kXcds = 8;
-
-// Key (row of the 32 x 32 output block) held in accumulator register r by
-// a lane of half h = lane / 32.
-__device__ __forceinline__ int block_key(int r, int h) {
-  return 8 * (r >> 2) + 4 * h + (r & 3);
-}
-
-// Hardware workgroup id -> logical id such that each XCD gets one
-// contiguous logical range (a bijection on [0, grid)).
-__device__ __forceinline__ int xcd_remap(int i, int grid) {
-  const int q = grid / kXcds, r = grid % kXcds;
-  const int x = i % kXcds, k = i / kXcds;
-  return x * q + (x < r ? x : r) + k;
-}
-
-__device__ __forceinline__ float exp2_fast(float x) {
-  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
-}
-
-// ---------------------------------------------------------------------------
-// bf16 operand plumbing.  BN = 64 keys per tile.
-//   LDS stage: K [BN][D + 8] row-major, V^T [D][BN + 8] with swapped key
-//   bits 2 and 3 (see the file header).  The +8 pads break bank conflicts
-//   between the 32 rows one 16-byte operand read touches.
-// ---------------------------------------------------------------------------
 template <int D>
-struct Bf16Path {
-  static constexpr int BN = 64;
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = BN + 8;
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int STAGE_BYTES = (BN * KSTR + D * VSTR) * 2;
-  static constexpr int CHUNKS = BN * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int KPT = CHUNKS;                    // V keys per thread (x 8 dims)
-  static_assert(KPT == 2 || KPT == 4, "unsupported tile shape");
-
-  struct QRegs { bf16x8_t q[D / 16]; };
-  struct Regs { u32x4_t k[CHUNKS]; u32x4_t v[KPT]; };
-
-  // Q^T as the B operand: lane holds query `row`, dims 16c + 8h .. +7.
-  static __device__ __forceinline__ void load_q(QRegs &qr, const uint16_t *qb,
-                                                long long rs, int row, int n, int h) {
-    const uint16_t *p = qb + (long long)row * rs + 8 * h;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row < n) x = *reinterpret_cast<const u32x4_t *>(p + 16 * c);
-      qr.q[c] = __builtin_bit_cast(bf16x8_t, x);
-    }
+struct Bf16Tile {
+  static constexpr int ROWB = D * 2;              // bytes per K/V row
+  static constexpr int TILE = kBN * ROWB;         // bytes per K (or V) tile
+  static constexpr int STAGE = 2 * TILE;          // K tile then V tile
+  static constexpr int LDS = kStages * STAGE;
+  static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
+  static constexpr int DPW = TILE / (1024 * kWaves);  // DMA instructions per wave per tensor
+  static_assert(DPW >= 1 && TILE % (1024 * kWaves) == 0, "tile / workgroup mismatch");
+  // K: rows read 16 at a time at one logical chunk -> spread over all slots.
+  static __device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
   }
-
-  // Global -> registers for the tile starting at key0; keys >= n read as 0.
-  static __device__ __forceinline__ void gload(Regs &rg, const uint16_t *kb,
-                                               const uint16_t *vb, long long rs,
-                                               int key0, int n, int tid) {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = key0 + row;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (key < n) x = *reinterpret_cast<const u32x4_t *>(kb + (long long)key * rs + col);
-      rg.k[i] = x;
-    }
-    const int dch = tid % (D / 8), kg = tid / (D / 8);
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int key = key0 + kg * KPT + j;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (key < n) x = *reinterpret_cast<const u32x4_t *>(vb + (long long)key * rs + dch * 8);
-      rg.v[j] = x;
-    }
-  }
-
-  // Registers -> LDS stage.  K row-major; V transposed with the key
-  // permutation pos(key) = key with bits 2 and 3 swapped.
-  static __device__ __forceinline__ void lstore(const Regs &rg, char *stage, int tid) {
-    uint16_t *lk = reinterpret_cast<uint16_t *>(stage);
-    uint16_t *lv = lk + K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4_t *>(lk + row * KSTR + col) = rg.k[i];
-    }
-    const int dch = tid % (D / 8), kg = tid / (D / 8);
-    const int key = kg * KPT;
-    const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      uint16_t *dst = lv + (dch * 8 + e) * VSTR + pos;
-      if constexpr (KPT == 4) {
-        u32x2_t w;
-        w[0] = __builtin_amdgcn_perm(rg.v[1][e >> 1], rg.v[0][e >> 1], sel);
-        w[1] = __builtin_amdgcn_perm(rg.v[3][e >> 1], rg.v[2][e >> 1], sel);
-        *reinterpret_cast<u32x2_t *>(dst) = w;
-      } else {
-        *reinterpret_cast<uint32_t *>(dst) =
-            __builtin_amdgcn_perm(rg.v[1][e >> 1], rg.v[0][e >> 1], sel);
-      }
-    }
-  }
-
-  // S^T (two 32-key blocks) = K . Q^T, fp32.
-  static __device__ __forceinline__ void scores(f32x16_t (&s)[2], const char *stage,
-                                                const QRegs &qr, int l32, int h) {
-    const uint16_t *lk = reinterpret_cast<const uint16_t *>(stage);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16_t acc = {};
-      const uint16_t *kr = lk + (32 * kb + l32) * KSTR + 8 * h;
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(kr + 16 * c);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr.q[c], acc, 0, 0, 0);
-      }
-      s[kb] = acc;
-    }
-  }
-
-  // O^T += V^T . P^T with P (already exponentiated) rounded to bf16.
-  static __device__ __forceinline__ void pv(f32x16_t (&o)[D / 32], const f32x16_t (&p)[2],
-                                            const char *stage, int l32, int h) {
-    const uint16_t *lv = reinterpret_cast<const uint16_t *>(stage) + K_ELEMS;
-    bf16x8_t pb[BN / 16];
-#pragma unroll
-    for (int c = 0; c < BN / 16; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)p[c >> 1][8 * (c & 1) + e];
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const uint16_t *vr = lv + (32 * db + l32) * VSTR + 8 * h;
-#pragma unroll
-      for (int c = 0; c < BN / 16; ++c) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(vr + 16 * c);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], o[db], 0, 0, 0);
-      }
-    }
-  }
-
-  // Four consecutive output dims d0..d0+3 of one row.
-  static __device__ __forceinline__ void store4(uint16_t *dst, float a, float b, float c,
-                                                float d) {
-    bf16x4_t x = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
-    *reinterpret_cast<bf16x4_t *>(dst) = x;
+  // V: four consecutive rows x 64 bytes per 32-lane transposed read.
+  static __device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? (10 * (r & 1) + 4 * ((r >> 1) & 1)) : (6 * ((r >> 1) & 1));
   }
 };
 
-// ---------------------------------------------------------------------------
-// fp32 operand plumbing.  BN = 32 keys per tile, K and V row-major in LDS.
-// v_mfma_f32_32x32x2_f32: lane l holds A[l % 32][l / 32] and B[l / 32][l % 32].
-// ---------------------------------------------------------------------------
-template <int D>
-struct F32Path {
-  static constexpr int BN = 32;
-  static constexpr int KSTR = D + 4;
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int STAGE_BYTES = 2 * BN * KSTR * 4;
-  static constexpr int CHUNKS = BN * D / 4 / kThreads;  // 16-byte chunks per thread, per tensor
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
 
-  struct QRegs { float q[D / 2]; };
-  struct Regs { u32x4_t k[CHUNKS]; u32x4_t v[CHUNKS]; };
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-  static __device__ __forceinline__ void load_q(QRegs &qr, const float *qb, long long rs,
-                                                int row, int n, int h) {
-    const float *p = qb + (long long)row * rs + h;
-#pragma unroll
-    for (int t = 0; t < D / 2; ++t) qr.q[t] = row < n ? p[2 * t] : 0.f;
-  }
+// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
-  static __device__ __forceinline__ void gload(Regs &rg, const float *kb, const float *vb,
-                                               long long rs, int key0, int n, int tid) {
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 4), col = (c % (D / 4)) * 4;
-      const int key = key0 + row;
-      u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-      if (key < n) {
-        x = *reinterpret_cast<const u32x4_t *>(kb + (long long)key * rs + col);
-        y = *reinterpret_cast<const u32x4_t *>(vb + (long long)key * rs + col);
-      }
-      rg.k[i] = x;
-      rg.v[i] = y;
-    }
-  }
+// Operand reads of the matrix-core phase are issued by hand: the compiler
+// cannot tell them apart from the LDS the in-flight global->LDS loads are
+// filling and would wait for those loads before every read.  Completion is
+// awaited with lgkm_wait, which is tied to the destination registers so no
+// consumer can be scheduled above it.
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_b64(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x2_t d;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
+  return d;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  u32x2_t d;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
+  return d;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2_t &a, u32x2_t &b, u32x2_t &c, u32x2_t &d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
 
-  static __device__ __forceinline__ void lstore(const Regs &rg, char *stage, int tid) {
-    float *lk = reinterpret_cast<float *>(stage);
-    float *lv = lk + K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / (D / 4), col = (c % (D / 4)) * 4;
-      *reinterpret_cast<u32x4_t *>(lk + row * KSTR + col) = rg.k[i];
-      *reinterpret_cast<u32x4_t *>(lv + row * KSTR + col) = rg.v[i];
-    }
-  }
+__device__ __forceinline__ bf16x8_t cat_bf16(u32x2_t lo, u32x2_t hi) {
+  const u32x4_t x = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8_t, x);
+}
 
-  static __device__ __forceinline__ void scores(f32x16_t (&s)[1], const char *stage,
-                                                const QRegs &qr, int l32, int h) {
-    const float *kr = reinterpret_cast<const float *>(stage) + l32 * KSTR + h;
-    f32x16_t acc = {};
-#pragma unroll
-    for (int t = 0; t < D / 2; ++t)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kr[2 * t], qr.q[t], acc, 0, 0, 0);
-    s[0] = acc;
-  }
+// Exchange with lane ^ 32: v_permlane32_swap swaps the upper half of its
+// first operand with the lower half of its second, so with both operands
+// holding x, lane l < 32 ends with (x[l], x[l+32]) and lane l >= 32 with
+// (x[l-32], x[l]): the pair is {own, partner} on every lane.  Issued by hand
+// on two distinct registers (the builtin, given the same value twice, is
+// folded as if the swap returned its inputs).
+__device__ __forceinline__ void pair_swap(float x, float &a, float &b) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), w = u;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(w));
+  a = __builtin_bit_cast(float, u);
+  b = __builtin_bit_cast(float, w);
+}
 
-  static __device__ __forceinline__ void pv(f32x16_t (&o)[D / 32], const f32x16_t (&p)[1],
-                                            const char *stage, int l32, int h) {
-    const float *lv = reinterpret_cast<const float *>(stage) + K_ELEMS;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float a = lv[block_key(r, h) * KSTR + 32 * db + l32];
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[0][r], o[db], 0, 0, 0);
-      }
-    }
-  }
+__device__ __forceinline__ float pair_max(float x) {  // max with lane ^ 32
+  float a, b;
+  pair_swap(x, a, b);
+  return fmaxf(a, b);
+}
 
-  static __device__ __forceinline__ void store4(float *dst, float a, float b, float c, float d) {
-    f32x4_t x = {a, b, c, d};
-    *reinterpret_cast<f32x4_t *>(dst) = x;
-  }
-};
+__device__ __forceinline__ float pair_sum(float x) {  // sum with lane ^ 32
+  float a, b;
+  pair_swap(x, a, b);
+  return a + b;
+}
 
-template <class T> struct PathFor;
-template <> struct PathFor<uint16_t> { template <int D> using type = Bf16Path<D>; };
-template <> struct PathFor<float> { template <int D> using type = F32Path<D>; };
-
-// ---------------------------------------------------------------------------
-// The forward kernel.
-// ---------------------------------------------------------------------------
-template <class T, int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(const FwdArgs a) {
-  using P = typename PathFor<T>::template type<D>;
-  constexpr int BN = P::BN;
-  constexpr int KB = BN / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * P::STAGE_BYTES];
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) {
+  using C = Bf16Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
+  const int grp = wv >> 2;  // ping-pong group
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  // --- work decomposition: (sequence, head, query tile) -------------------
-  const int L = xcd_remap(blockIdx.x, a.grid);
-  const int bh = L / a.n_qtiles;
-  const int qt = a.n_qtiles - 1 - (L - bh * a.n_qtiles);  // heaviest first
-  const int s = bh / a.H;
-  const int hd = bh - s * a.H;
-  int n;
-  long long base, lbase;
-  if constexpr (VARLEN) {
-    const int t0 = a.cu_seqlens[s];
-    n = a.cu_seqlens[s + 1] - t0;
-    base = (long long)t0 * a.row_stride;
-    lbase = (long long)t0 * a.lse_row_stride;
-  } else {
-    n = a.n;
-    base = (long long)s * a.seq_stride;
-    lbase = (long long)s * a.lse_seq_stride;
-  }
-  base += (long long)hd * a.head_stride;
-  lbase += (long long)hd * a.lse_head_stride;
-
-  const int m0 = qt * kBlockM;
+  const TileCoords tc = tile_coords<VARLEN>(a, kBlockM);
+  const int n = tc.n, m0 = tc.m0;
   if (m0 >= n) return;  // uniform over the workgroup, before any barrier
 
-  const T *qb = reinterpret_cast<const T *>(a.q) + base;
-  const T *kb = reinterpret_cast<const T *>(a.k) + base;
-  const T *vb = reinterpret_cast<const T *>(a.v) + base;
+  const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + tc.base;
+  const uint16_t *kb = reinterpret_cast<const uint16_t *>(a.k) + tc.base;
+  const uint16_t *vb = reinterpret_cast<const uint16_t *>(a.v) + tc.base;
   const long long rs = a.row_stride;
 
   const int n_kv = CAUSAL ? (n < m0 + kBlockM ? n : m0 + kBlockM) : n;
-  const int nt = (n_kv + BN - 1) / BN;
-  const int qw0 = m0 + 32 * wv;  // first query row of this wave
-  const int qrow = qw0 + l32;    // this lane's query row
-  const bool wave_live = qw0 < n;
+  const int T = (n_kv + kBN - 1) / kBN;  // K/V tiles of the workgroup
+  const int qw0 = m0 + 32 * wv;          // first query row of this wave
+  const int qrow = qw0 + l32;            // this lane's query row
+  // tiles this wave works on (causal: none entirely above its diagonal)
+  int Tw = 0;
+  if (qw0 < n) Tw = CAUSAL ? ((qw0 + 31) / kBN + 1 < T ? (qw0 + 31) / kBN + 1 : T) : T;
 
-  // --- initialise: resident Q, m = -inf, l = 0, O = 0 -----------------------
-  typename P::QRegs qr;
-  P::load_q(qr, qb, rs, qrow, n, h);
-  float m_run = -__builtin_huge_valf();
-  float l_run = 0.f;  // this lane's partial row sum (its half of the keys)
+  // ---- resident Q^T (B operand): lane holds Q[qrow][16c + 8h .. +7] ---------
+  bf16x8_t q[D / 16];
+  {
+    const uint16_t *p = qb + (long long)qrow * rs + 8 * h;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (qrow < n) x = *reinterpret_cast<const u32x4_t *>(p + 16 * c);
+      q[c] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+  // ---- direct global -> LDS loads: slot p of a tile <- row p / CPR ---------
+  int d_row[C::DPW], d_colk[C::DPW], d_colv[C::DPW];
+#pragma unroll
+  for (int i = 0; i < C::DPW; ++i) {
+    const int p = (wv * C::DPW + i) * kWave + lane;
+    const int row = p / C::CPR, slot = p % C::CPR;
+    d_row[i] = row;
+    d_colk[i] = 8 * (slot ^ C::swz_k(row));
+    d_colv[i] = 8 * (slot ^ C::swz_v(row));
+  }
+  auto issue_tile = [&](int t) {
+    char *st = smem + (t & (kStages - 1)) * C::STAGE;
+    const int key0 = t * kBN;
+#pragma unroll
+    for (int i = 0; i < C::DPW; ++i) {
+      int key = key0 + d_row[i];
+      key = key < n ? key : n - 1;  // rows past the end: any valid row, masked later
+      const long long ro = (long long)key * rs;
+      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(kb + ro + d_colk[i]),
+                                       (FA_LDS void *)(st + (wv * C::DPW + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(vb + ro + d_colv[i]),
+                                       (FA_LDS void *)(st + C::TILE + (wv * C::DPW + i) * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  // ---- LDS operand addresses (byte offsets within a stage) ----------------
+  // K operand (kb, c): row 32 kb + l32, logical chunk 2c + h.
+  uint32_t kofs[D / 16];
+  {
+    const int sw = C::swz_k(l32);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) kofs[c] = l32 * C::ROWB + 16 * ((2 * c + h) ^ sw);
+  }
+  // V^T operand (db, c): this lane addresses key row 16c (+8) + 4h + e4 at
+  // d = 32 db + 16 g + 4 (j % 4) .. +3 (j = lane % 16, e4 = j / 4, g = lane / 16 % 2).
+  uint32_t vofs[D / 32];
+  {
+    const int j = lane & 15, e4 = j >> 2, g = (lane >> 4) & 1;
+    const int sw = C::swz_v(e4);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      vofs[db] = C::TILE + (4 * h + e4) * C::ROWB +
+                 16 * ((4 * db + 2 * g + ((j & 3) >> 1)) ^ sw) + 8 * (j & 1);
+  }
+  const uint32_t lds_base =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS char *)smem));
+
+  // ---- running state ------------------------------------------------------
+  float m_ref = neg_inf();  // exponent reference (raw score units)
+  float l_run = 0.f;        // this lane's partial row sum (its half of the keys)
   f32x16_t o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
+  f32x16_t sc[2];
+  bf16x8_t pb[kBN / 16];
   const float sl2 = a.scale_log2;
+  const float lazy_thr = a.lazy_thr;
 
-  typename P::Regs rg;
-  P::gload(rg, kb, vb, rs, 0, n, tid);
-  P::lstore(rg, smem, tid);
-
-  // --- main loop over K/V tiles --------------------------------------------
-  for (int kt = 0; kt < nt; ++kt) {
-    const bool more = kt + 1 < nt;
-    if (more) P::gload(rg, kb, vb, rs, (kt + 1) * BN, n, tid);
-    __syncthreads();
-    const char *stage = smem + (kt & 1) * P::STAGE_BYTES;
-    const int key0 = kt * BN;
-    const bool active = wave_live && (!CAUSAL || key0 <= qw0 + 31);
-    if (active) {
-      f32x16_t sc[KB];
-      P::scores(sc, stage, qr, l32, h);
-
-      // mask keys past the end and, in causal mode, keys after the query
-      const bool need_mask = (key0 + BN > n) || (CAUSAL && key0 + BN - 1 > qw0);
-      if (need_mask) {
+  // M(t): S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T, interleaved.  Step i
+  // does S product (kb = i % 2, c = i / 2) and P.V product (db = i / 4,
+  // c = i % 4); the operands of step i + 1 are read while step i computes.
+  constexpr int NSTEP = D / 8;
+  auto m_body = [&](auto do_s, auto do_pv, uint32_t kbase, uint32_t vbase) {
+    constexpr bool S = decltype(do_s)::value, PV = decltype(do_pv)::value;
+    uint32_t ka[D / 16], va[D / 32];
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
+    for (int c = 0; c < D / 16; ++c) ka[c] = kbase + kofs[c];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * b + block_key(r, h);
-            const bool ok = key < n && (!CAUSAL || key <= qrow);
-            if (!ok) sc[b][r] = -__builtin_huge_valf();
-          }
+    for (int db = 0; db < D / 32; ++db) va[db] = vbase + vofs[db];
+    u32x2_t kr[2][2], vr[2][2];
+    auto issue = [&](auto I) {
+      constexpr int i = decltype(I)::value, b = i & 1;
+      if constexpr (S) {
+        constexpr int kbk = i & 1, c = i >> 1;
+        kr[b][0] = lds_read_b64<kbk * 32 * C::ROWB>(ka[c]);
+        kr[b][1] = lds_read_b64<kbk * 32 * C::ROWB + 8>(ka[c]);
+      } else {
+        kr[b][0] = kr[b][1] = u32x2_t{0u, 0u};
       }
+      if constexpr (PV) {
+        constexpr int db = i >> 2, c = i & 3;
+        vr[b][0] = lds_read_tr16<16 * c * C::ROWB>(va[db]);
+        vr[b][1] = lds_read_tr16<(16 * c + 8) * C::ROWB>(va[db]);
+      } else {
+        vr[b][0] = vr[b][1] = u32x2_t{0u, 0u};
+      }
+    };
+    issue(std::integral_constant<int, 0>{});
+    static_for<NSTEP>([&](auto I) {
+      constexpr int i = decltype(I)::value, b = i & 1;
+      if constexpr (i + 1 < NSTEP) issue(std::integral_constant<int, i + 1>{});
+      constexpr int in_flight = (i + 1 < NSTEP) ? (S ? 2 : 0) + (PV ? 2 : 0) : 0;
+      lgkm_wait<in_flight>(kr[b][0], kr[b][1], vr[b][0], vr[b][1]);
+      if constexpr (S) {
+        constexpr int kbk = i & 1, c = i >> 1;
+        sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_bf16(kr[b][0], kr[b][1]), q[c],
+                                                          c == 0 ? f32x16_t{} : sc[kbk], 0, 0, 0);
+      }
+      if constexpr (PV) {
+        constexpr int db = i >> 2, c = i & 3;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_bf16(vr[b][0], vr[b][1]), pb[c], o[db],
+                                                        0, 0, 0);
+      }
+    });
+  };
+  auto m_phase = [&](int t) {
+    const bool do_s = t < Tw;
+    const bool do_pv = t >= 1 && t <= Tw;
+    if (!do_s && !do_pv) return;
+    const uint32_t kbase = lds_base + (t & (kStages - 1)) * C::STAGE;
+    const uint32_t vbase = lds_base + ((t - 1) & (kStages - 1)) * C::STAGE;
+    __builtin_amdgcn_s_setprio(1);
+    if (do_s && do_pv)
+      m_body(std::true_type{}, std::true_type{}, kbase, vbase);
+    else if (do_s)
+      m_body(std::true_type{}, std::false_type{}, kbase, vbase);
+    else
+      m_body(std::false_type{}, std::true_type{}, kbase, vbase);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-      // online softmax: row max over this tile (in-lane, then lane ^ 32)
-      float mx = sc[0][0];
+  // V(t): softmax update of S_t -> P_t (bf16), l, rescaled O.
+  auto v_phase = [&](int t) {
+    if (t >= Tw) return;
+    const int key0 = t * kBN;
+    if ((key0 + kBN > n) || (CAUSAL && key0 + kBN - 1 > qw0)) {
 #pragma unroll
-      for (int b = 0; b < KB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_ref = (m_new == -__builtin_huge_valf()) ? 0.f : m_new;  // ghost-row guard
-      const float alpha = exp2_fast((m_run - m_ref) * sl2);
-      const float mb = m_ref * sl2;
-      float ps = 0.f;
-#pragma unroll
-      for (int b = 0; b < KB; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(__builtin_fmaf(sc[b][r], sl2, -mb));
-          sc[b][r] = p;
-          ps += p;
+          const int key = key0 + 32 * b + block_key(r, h);
+          if (!(key < n && (!CAUSAL || key <= qrow))) sc[b][r] = neg_inf();
         }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
+    }
+    float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+    mx = pair_max(mx);
+    const bool bump = mx > m_ref + lazy_thr;  // also true on the first finite tile
+    float alpha = 1.f;
+    if (bump) {
+      alpha = exp2_fast((m_ref - mx) * sl2);  // 0 when m_ref = -inf
+      m_ref = mx;
+    }
+    const float mb = (m_ref == neg_inf() ? 0.f : m_ref) * sl2;  // ghost-row guard
+    float ps = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_fast(__builtin_fmaf(sc[b][r], sl2, -mb));
+        sc[b][r] = p;
+        ps += p;
+      }
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-
-      P::pv(o, sc, stage, l32, h);
     }
-    if (more) P::lstore(rg, smem + ((kt + 1) & 1) * P::STAGE_BYTES, tid);
+    l_run = l_run * alpha + ps;
+#pragma unroll
+    for (int c = 0; c < kBN / 16; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)sc[c >> 1][8 * (c & 1) + e];
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, tile 0 landed ---------------------
+  issue_tile(0);
+  if (T > 1) {
+    issue_tile(1);
+    wait_vmem<2 * C::DPW>();
+  } else {
+    wait_vmem<0>();
+  }
+  wg_barrier();
+
+  // ---- ping-pong loop: phase ph; group g runs step ph - g ------------------
+  for (int ph = 0; ph <= 2 * T + 1; ++ph) {
+    const int t2 = ph >> 1;
+    const bool odd = ph & 1;
+    if (!odd && t2 + 2 < T) issue_tile(t2 + 2);  // stage of tile t2 - 2, free since ph - 1
+    const int step = ph - grp;
+    if (step >= 0) {
+      if (!(step & 1))
+        m_phase(step >> 1);
+      else
+        v_phase(step >> 1);
+    }
+    if (odd) {  // tile t2 + 1 must have landed before phase ph + 1
+      if (t2 + 2 < T)
+        wait_vmem<2 * C::DPW>();
+      else
+        wait_vmem<0>();
+    }
+    wg_barrier();
   }
 
-  // --- finalise: O / l, lse = scale * m + ln l --------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- finalise: O / l, lse = scale * m + ln l --------------------------------
+  const float l_tot = pair_sum(l_run);
   if (qrow < n) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    T *orow = reinterpret_cast<T *>(a.o) + base + (long long)qrow * rs;
+    uint16_t *orow = reinterpret_cast<uint16_t *>(a.o) + tc.base + (long long)qrow * rs;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        P::store4(orow + 32 * db + 8 * g + 4 * h, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
-                  o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      for (int gq = 0; gq < 4; ++gq) {
+        const bf16x4_t x = {(__bf16)(o[db][4 * gq] * inv), (__bf16)(o[db][4 * gq + 1] * inv),
+                            (__bf16)(o[db][4 * gq + 2] * inv), (__bf16)(o[db][4 * gq + 3] * inv)};
+        *reinterpret_cast<bf16x4_t *>(orow + 32 * db + 8 * gq + 4 * h) = x;
+      }
     if (a.lse != nullptr && h == 0) {
-      const float m_fin = (m_run == -__builtin_huge_valf()) ? 0.f : m_run;
-      a.lse[lbase + (long long)qrow * a.lse_row_stride] =
-          l_tot > 0.f ? m_fin * a.scale + __logf(l_tot) : -__builtin_huge_valf();
+      const float m_fin = (m_ref == neg_inf()) ? 0.f : m_ref;
+      a.lse[tc.lbase + (long long)qrow * a.lse_row_stride] =
+          l_tot > 0.f ? m_fin * a.scale + __logf(l_tot) : neg_inf();
     }
   }
 }
 
-template <class T, int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D, CAUSAL, VARLEN>), dim3(a.grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3(a.grid), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <class T, int D>
+template <int D>
 hipError_t launch_d(const FwdArgs &a, bool causal, bool varlen, hipStream_t stream) {
   if (causal)
-    return varlen ? launch<T, D, true, true>(a, stream) : launch<T, D, true, false>(a, stream);
-  return varlen ? launch<T, D, false, true>(a, stream) : launch<T, D, false, false>(a, stream);
-}
-
-template <class T>
-hipError_t launch_t(const FwdArgs &a, int d, bool causal, bool varlen, hipStream_t stream) {
-  if (d == 64) return launch_d<T, 64>(a, causal, varlen, stream);
-  if (d == 128) return launch_d<T, 128>(a, causal, varlen, stream);
-  return hipErrorInvalidValue;
+    return varlen ? launch<D, true, true>(a, stream) : launch<D, true, false>(a, stream);
+  return varlen ? launch<D, false, true>(a, stream) : launch<D, false, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs &a, int dtype, int d, bool causal, bool varlen,
+hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
                       hipStream_t stream) {
-  if (dtype == 0) return launch_t<float>(a, d, causal, varlen, stream);
-  if (dtype == 1) return launch_t<uint16_t>(a, d, causal, varlen, stream);
+  if (dtype == 0) return launch_fwd_f32(a, d, causal, varlen, stream);
+  if (dtype != 1) return hipErrorInvalidValue;
+  a.n_qtiles = (a.max_len + kBlockM - 1) / kBlockM;
+  const long long grid = (long long)a.batch * a.H * a.n_qtiles;
+  if (grid > 0x7fffffffll || grid <= 0) return hipErrorInvalidValue;
+  a.grid = (int)grid;
+  a.lazy_thr = 8.0f / a.scale_log2;  // weights stay <= 2^8 between rescales
+  if (d == 64) return launch_d<64>(a, causal, varlen, stream);
+  if (d == 128) return launch_d<128>(a, causal, varlen, stream);
   return hipErrorInvalidValue;
 }
 

@@ -1,6 +1,6 @@
 // fa_fwd_launch.h -- internal interface between the C ABI (fa355_api.hip)
-// and the forward kernels (fa_fwd_kernel.hip).  Not installed, not part of
-// the public ABI.
+// and the forward kernels (fa_fwd_kernel.hip, fa_fwd_f32.hip).  Not
+// installed, not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,19 +27,26 @@ struct FwdArgs {
   long long lse_head_stride;
   long long lse_row_stride;
   int n;         // sequence length (fixed-length batches)
+  int batch;     // sequences (B, or nseq for a packed batch)
   int H;         // heads
-  int n_qtiles;  // query tiles per (sequence, head)
-  int grid;      // workgroups launched
+  int max_len;   // longest sequence (sizes the grid)
+  int n_qtiles;  // query tiles per (sequence, head)  -- set by the launcher
+  int grid;      // workgroups launched                -- set by the launcher
   float scale;       // softmax scale applied to q.k
   float scale_log2;  // scale * log2(e), for exp2
+  float lazy_thr;    // raw-score slack of the exponent reference (bf16 kernel)
 };
 
-// Query rows per workgroup.
-constexpr int kBlockM = 128;
+// Smallest number of query rows any kernel gives one workgroup (used by the
+// host to bound the grid size before dispatch).
+constexpr int kMinBlockM = 128;
 
 // Enqueue the forward kernel for (dtype, d, causal, varlen).  Returns the
 // HIP status of the launch.
-hipError_t launch_fwd(const FwdArgs &a, int dtype, int d, bool causal,
-                      bool varlen, hipStream_t stream);
+hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
+                      hipStream_t stream);
+
+// The fp32 kernel (fa_fwd_f32.hip).
+hipError_t launch_fwd_f32(FwdArgs a, int d, bool causal, bool varlen, hipStream_t stream);
 
 }  // namespace fa355
