@@ -127,8 +127,8 @@ def cpu_baseline(w, inp, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=fa_inputs.HEADLINE.name,
                     choices=[w.name for w in fa_inputs.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -31,8 +31,11 @@
 // 16c + 8(e/4) + 4(l/32) + e%4, which is what lane l holds.
 //
 // LDS: K and V tiles stay row-major ([key][d], as in memory) in a 4-stage
-// ring filled by direct global->LDS loads (global_load_lds_dwordx4) issued
-// two tiles ahead, so no registers stage them.  Operands are read with
+// ring.  Each wave moves 1/8 of every tile: its matrix phase M(t) starts by
+// issuing the global loads of tile t + 2 into registers, and its softmax phase
+// V(t) writes them into LDS, so global latency is hidden behind a phase.
+// (Direct global->LDS loads were tried: on this part each one stalls the
+// issuing wave for about 100 cycles.)  Operands are read with
 // 64-bit LDS reads: K as two ds_read_b64 per 16-byte operand, V^T with
 // ds_read_b64_tr_b16, which hands each lane one d column of four key rows
 // (lanes 4e..4e+3 of a 16-lane group address row e, lane i receives element
@@ -66,6 +69,23 @@
 namespace fa355 {
 namespace {
 
+// Tuning knobs (compile-time): wave priority during the matrix and softmax
+// phases, and how many matrix steps ahead operands are read.
+#ifndef FA_PRIO_M
+#define FA_PRIO_M 3
+#endif
+#ifndef FA_PRIO_V
+#define FA_PRIO_V 0
+#endif
+#ifndef FA_LOOKAHEAD
+#define FA_LOOKAHEAD 3
+#endif
+// K/V staging: 0 = global loads of tile t + 2 issued in M(t), written to LDS
+// in V(t); 1 = loads of tile t + 1 issued in V(t - 1), written in M(t).
+#ifndef FA_STORE_IN_M
+#define FA_STORE_IN_M 0
+#endif
+
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;  // 512
 constexpr int kBlockM = 32 * kWaves;      // 256 query rows
@@ -91,15 +111,9 @@ struct Bf16Tile {
   }
 };
 
-// Wait until at most N vector-memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
-}
-
+// Workgroup barrier that also completes this wave's LDS writes first.
 __device__ __forceinline__ void wg_barrier() {
-  asm volatile("" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -137,6 +151,24 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x2_t &a, u32x2_t &b, u32x2_t &c, u32x2_t &d) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
 }
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2_t &a, u32x2_t &b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// v_max3_f32 / v_max_f32 without the NaN-quieting canonicalisation the
+// compiler adds to fmaxf on values it cannot prove canonical (scores are
+// never NaN for finite inputs).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 __device__ __forceinline__ bf16x8_t cat_bf16(u32x2_t lo, u32x2_t hi) {
   const u32x4_t x = {lo[0], lo[1], hi[0], hi[1]};
@@ -159,7 +191,7 @@ __device__ __forceinline__ void pair_swap(float x, float &a, float &b) {
 __device__ __forceinline__ float pair_max(float x) {  // max with lane ^ 32
   float a, b;
   pair_swap(x, a, b);
-  return fmaxf(a, b);
+  return max2f(a, b);
 }
 
 __device__ __forceinline__ float pair_sum(float x) {  // sum with lane ^ 32
@@ -209,29 +241,52 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     }
   }
 
-  // ---- direct global -> LDS loads: slot p of a tile <- row p / CPR ---------
-  int d_row[C::DPW], d_colk[C::DPW], d_colv[C::DPW];
+  // ---- K/V tile staging: global -> registers -> LDS ---------------------
+  // A tile is 2 * TILE bytes of LDS, 16-byte slots; slot p holds row p / CPR.
+  // Wave wv owns slots (wv * DPW + i) * 64 + lane: it loads them into
+  // registers in its M(t) phase and writes them in its next M phase.
+  int d_row[C::DPW];
+  const uint16_t *d_pk[C::DPW], *d_pv[C::DPW];  // source of the slot in tile 0
+  const uint16_t *d_ck[C::DPW], *d_cv[C::DPW];  // its column in row 0 (ragged path)
 #pragma unroll
   for (int i = 0; i < C::DPW; ++i) {
     const int p = (wv * C::DPW + i) * kWave + lane;
     const int row = p / C::CPR, slot = p % C::CPR;
     d_row[i] = row;
-    d_colk[i] = 8 * (slot ^ C::swz_k(row));
-    d_colv[i] = 8 * (slot ^ C::swz_v(row));
+    d_ck[i] = kb + 8 * (slot ^ C::swz_k(row));
+    d_cv[i] = vb + 8 * (slot ^ C::swz_v(row));
+    d_pk[i] = d_ck[i] + (long long)row * rs;
+    d_pv[i] = d_cv[i] + (long long)row * rs;
   }
-  auto issue_tile = [&](int t) {
-    char *st = smem + (t & (kStages - 1)) * C::STAGE;
+  u32x4_t stg[2 * C::DPW];  // this wave's slots of the tile in flight: K then V
+  auto load_tile = [&](int t_) {
+    const int t = __builtin_amdgcn_readfirstlane(t_);
     const int key0 = t * kBN;
+    if (key0 + kBN <= n) {  // whole tile in range: one 64-bit add per load
+      const long long off = (long long)key0 * rs;
+#pragma unroll
+      for (int i = 0; i < C::DPW; ++i) {
+        stg[i] = *reinterpret_cast<const u32x4_t *>(d_pk[i] + off);
+        stg[C::DPW + i] = *reinterpret_cast<const u32x4_t *>(d_pv[i] + off);
+      }
+    } else {  // ragged last tile: rows past the end read row n - 1 (masked later)
+#pragma unroll
+      for (int i = 0; i < C::DPW; ++i) {
+        int key = key0 + d_row[i];
+        key = key < n ? key : n - 1;
+        const long long ro = (long long)key * rs;
+        stg[i] = *reinterpret_cast<const u32x4_t *>(d_ck[i] + ro);
+        stg[C::DPW + i] = *reinterpret_cast<const u32x4_t *>(d_cv[i] + ro);
+      }
+    }
+  };
+  auto store_tile = [&](int t_) {
+    const int t = __builtin_amdgcn_readfirstlane(t_);
+    char *st = smem + (t & (kStages - 1)) * C::STAGE + (wv * C::DPW) * 1024 + lane * 16;
 #pragma unroll
     for (int i = 0; i < C::DPW; ++i) {
-      int key = key0 + d_row[i];
-      key = key < n ? key : n - 1;  // rows past the end: any valid row, masked later
-      const long long ro = (long long)key * rs;
-      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(kb + ro + d_colk[i]),
-                                       (FA_LDS void *)(st + (wv * C::DPW + i) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(vb + ro + d_colv[i]),
-                                       (FA_LDS void *)(st + C::TILE + (wv * C::DPW + i) * 1024),
-                                       16, 0, 0);
+      *reinterpret_cast<u32x4_t *>(st + i * 1024) = stg[i];
+      *reinterpret_cast<u32x4_t *>(st + C::TILE + i * 1024) = stg[C::DPW + i];
     }
   };
 
@@ -270,39 +325,43 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
 
   // M(t): S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T, interleaved.  Step i
   // does S product (kb = i % 2, c = i / 2) and P.V product (db = i / 4,
-  // c = i % 4); the operands of step i + 1 are read while step i computes.
+  // c = i % 4); operands are read kLook steps ahead into a ring of buffers.
   constexpr int NSTEP = D / 8;
+  constexpr int kLook = FA_LOOKAHEAD;
+  constexpr int NB = kLook + 1;
   auto m_body = [&](auto do_s, auto do_pv, uint32_t kbase, uint32_t vbase) {
     constexpr bool S = decltype(do_s)::value, PV = decltype(do_pv)::value;
+    constexpr int RPS = (S ? 2 : 0) + (PV ? 2 : 0);  // LDS reads per step
     uint32_t ka[D / 16], va[D / 32];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) ka[c] = kbase + kofs[c];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) va[db] = vbase + vofs[db];
-    u32x2_t kr[2][2], vr[2][2];
+    u32x2_t kr[NB][2], vr[NB][2];
     auto issue = [&](auto I) {
-      constexpr int i = decltype(I)::value, b = i & 1;
+      constexpr int i = decltype(I)::value, b = i % NB;
       if constexpr (S) {
         constexpr int kbk = i & 1, c = i >> 1;
         kr[b][0] = lds_read_b64<kbk * 32 * C::ROWB>(ka[c]);
         kr[b][1] = lds_read_b64<kbk * 32 * C::ROWB + 8>(ka[c]);
-      } else {
-        kr[b][0] = kr[b][1] = u32x2_t{0u, 0u};
       }
       if constexpr (PV) {
         constexpr int db = i >> 2, c = i & 3;
         vr[b][0] = lds_read_tr16<16 * c * C::ROWB>(va[db]);
         vr[b][1] = lds_read_tr16<(16 * c + 8) * C::ROWB>(va[db]);
-      } else {
-        vr[b][0] = vr[b][1] = u32x2_t{0u, 0u};
       }
     };
-    issue(std::integral_constant<int, 0>{});
+    static_for<(kLook < NSTEP ? kLook : NSTEP)>([&](auto I) { issue(I); });
     static_for<NSTEP>([&](auto I) {
-      constexpr int i = decltype(I)::value, b = i & 1;
-      if constexpr (i + 1 < NSTEP) issue(std::integral_constant<int, i + 1>{});
-      constexpr int in_flight = (i + 1 < NSTEP) ? (S ? 2 : 0) + (PV ? 2 : 0) : 0;
-      lgkm_wait<in_flight>(kr[b][0], kr[b][1], vr[b][0], vr[b][1]);
+      constexpr int i = decltype(I)::value, b = i % NB;
+      if constexpr (i + kLook < NSTEP) issue(std::integral_constant<int, i + kLook>{});
+      constexpr int ahead = (NSTEP - 1 - i) < kLook ? (NSTEP - 1 - i) : kLook;
+      if constexpr (S && PV)
+        lgkm_wait<RPS * ahead>(kr[b][0], kr[b][1], vr[b][0], vr[b][1]);
+      else if constexpr (S)
+        lgkm_wait<RPS * ahead>(kr[b][0], kr[b][1]);
+      else
+        lgkm_wait<RPS * ahead>(vr[b][0], vr[b][1]);
       if constexpr (S) {
         constexpr int kbk = i & 1, c = i >> 1;
         sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_bf16(kr[b][0], kr[b][1]), q[c],
@@ -315,24 +374,39 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       }
     });
   };
+  // M(t) first issues the global loads of this wave's share of tile t + 2 (the
+  // staging registers are free: their last LDS write finished before the
+  // previous barrier).
   auto m_phase = [&](int t) {
     const bool do_s = t < Tw;
     const bool do_pv = t >= 1 && t <= Tw;
+#if FA_STORE_IN_M
+    if (t >= 1 && t + 1 < T) store_tile(t + 1);
+#else
+    if (t + 2 < T) load_tile(t + 2);
+#endif
     if (!do_s && !do_pv) return;
     const uint32_t kbase = lds_base + (t & (kStages - 1)) * C::STAGE;
     const uint32_t vbase = lds_base + ((t - 1) & (kStages - 1)) * C::STAGE;
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(FA_PRIO_M);
     if (do_s && do_pv)
       m_body(std::true_type{}, std::true_type{}, kbase, vbase);
     else if (do_s)
       m_body(std::true_type{}, std::false_type{}, kbase, vbase);
     else
       m_body(std::false_type{}, std::true_type{}, kbase, vbase);
-    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(FA_PRIO_V);
   };
 
   // V(t): softmax update of S_t -> P_t (bf16), l, rescaled O.
+  // V(t) also writes this wave's share of tile t + 2 (loaded during M(t)) into
+  // its LDS stage, whose previous tile t - 2 was last read two phases earlier.
   auto v_phase = [&](int t) {
+#if FA_STORE_IN_M
+    if (t + 2 < T) load_tile(t + 2);
+#else
+    if (t + 2 < T) store_tile(t + 2);
+#endif
     if (t >= Tw) return;
     const int key0 = t * kBN;
     if ((key0 + kBN > n) || (CAUSAL && key0 + kBN - 1 > qw0)) {
@@ -344,9 +418,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
           if (!(key < n && (!CAUSAL || key <= qrow))) sc[b][r] = neg_inf();
         }
     }
-    float mx = fmaxf(sc[0][0], sc[1][0]);
+    // row max: four independent max3 chains over 8 scores each, then combined
+    float mq[4];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+    for (int j = 0; j < 4; ++j) {
+      const int b = j >> 1, r0 = 8 * (j & 1);
+      float m = max3f(sc[b][r0], sc[b][r0 + 1], sc[b][r0 + 2]);
+      m = max3f(m, sc[b][r0 + 3], sc[b][r0 + 4]);
+      m = max3f(m, sc[b][r0 + 5], sc[b][r0 + 6]);
+      mq[j] = max2f(m, sc[b][r0 + 7]);
+    }
+    float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
     mx = pair_max(mx);
     const bool bump = mx > m_ref + lazy_thr;  // also true on the first finite tile
     float alpha = 1.f;
@@ -355,15 +437,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       m_ref = mx;
     }
     const float mb = (m_ref == neg_inf() ? 0.f : m_ref) * sl2;  // ghost-row guard
-    float ps = 0.f;
+    float pq[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums (short add chains)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_fast(__builtin_fmaf(sc[b][r], sl2, -mb));
         sc[b][r] = p;
-        ps += p;
+        pq[(r & 1) + 2 * b] += p;
       }
+    const float ps = (pq[0] + pq[1]) + (pq[2] + pq[3]);
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
@@ -375,33 +458,23 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)sc[c >> 1][8 * (c & 1) + e];
   };
 
-  // ---- prologue: tiles 0 and 1 in flight, tile 0 landed ---------------------
-  issue_tile(0);
+  // ---- prologue: tiles 0 and 1 in LDS ---------------------------------------
+  load_tile(0);
+  store_tile(0);
   if (T > 1) {
-    issue_tile(1);
-    wait_vmem<2 * C::DPW>();
-  } else {
-    wait_vmem<0>();
+    load_tile(1);
+    store_tile(1);
   }
   wg_barrier();
 
   // ---- ping-pong loop: phase ph; group g runs step ph - g ------------------
   for (int ph = 0; ph <= 2 * T + 1; ++ph) {
-    const int t2 = ph >> 1;
-    const bool odd = ph & 1;
-    if (!odd && t2 + 2 < T) issue_tile(t2 + 2);  // stage of tile t2 - 2, free since ph - 1
     const int step = ph - grp;
     if (step >= 0) {
       if (!(step & 1))
         m_phase(step >> 1);
       else
         v_phase(step >> 1);
-    }
-    if (odd) {  // tile t2 + 1 must have landed before phase ph + 1
-      if (t2 + 2 < T)
-        wait_vmem<2 * C::DPW>();
-      else
-        wait_vmem<0>();
     }
     wg_barrier();
   }
