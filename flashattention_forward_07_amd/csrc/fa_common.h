@@ -26,12 +26,30 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 // register r by a lane of half h = lane / 32.
 __device__ __forceinline__ int block_key(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Hardware workgroup id -> logical id such that each XCD receives one
-// contiguous logical range (a bijection on [0, grid)).
-__device__ __forceinline__ int xcd_remap(int i, int grid) {
-  const int q = grid / kXcds, r = grid % kXcds;
-  const int x = i % kXcds, k = i / kXcds;
-  return x * q + (x < r ? x : r) + k;
+// Hardware workgroup id -> (head index bh, query-tile level qi), a bijection
+// on [0, grid).  Workgroups are dispatched round-robin over the XCDs
+// (hardware id i runs on XCD i % 8, as its (i / 8)-th workgroup there).  When
+// the number of (sequence, head) pairs is a multiple of 8, head h is pinned
+// to XCD h % 8, so all query tiles of a head share that XCD's L2 and its
+// K/V stream, and each XCD issues its tiles level by level, heaviest
+// (highest query tile) first across its heads, which balances the causal
+// triangle.  Otherwise the order is heaviest-first over all heads.
+struct TileOrder {
+  int bh;  // (sequence, head) pair
+  int qi;  // 0 = heaviest query tile
+};
+__device__ __forceinline__ TileOrder tile_order(int i, int n_heads) {
+  TileOrder o;
+  if (n_heads % kXcds == 0) {
+    const int hx = n_heads / kXcds;  // heads per XCD
+    const int x = i % kXcds, r = i / kXcds;
+    o.bh = x + kXcds * (r % hx);
+    o.qi = r / hx;
+  } else {
+    o.bh = i % n_heads;
+    o.qi = i / n_heads;
+  }
+  return o;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) {
@@ -48,13 +66,12 @@ struct TileCoords {
   long long lbase;  // lse offset of (sequence, head) token 0
 };
 
-// Logical workgroup -> (sequence, head, query tile); query tiles of one head
-// are issued heaviest (last rows) first.
+// Workgroup -> (sequence, head, query tile) in the order of tile_order.
 template <bool VARLEN>
 __device__ __forceinline__ TileCoords tile_coords(const FwdArgs &a, int block_m) {
-  const int L = xcd_remap(blockIdx.x, a.grid);
-  const int bh = L / a.n_qtiles;
-  const int qt = a.n_qtiles - 1 - (L - bh * a.n_qtiles);
+  const TileOrder to = tile_order(blockIdx.x, a.batch * a.H);
+  const int bh = to.bh;
+  const int qt = a.n_qtiles - 1 - to.qi;
   const int s = bh / a.H;
   const int hd = bh - s * a.H;
   TileCoords c;
