@@ -35,19 +35,23 @@
 // issuing the global loads of tile t + 2 into registers, and its softmax phase
 // V(t) writes them into LDS, so global latency is hidden behind a phase.
 // (Direct global->LDS loads were tried: on this part each one stalls the
-// issuing wave for about 100 cycles.)  Operands are read with
-// 64-bit LDS reads: K as two ds_read_b64 per 16-byte operand, V^T with
-// ds_read_b64_tr_b16, which hands each lane one d column of four key rows
-// (lanes 4e..4e+3 of a 16-lane group address row e, lane i receives element
-// i of each row).  16-byte chunks are XOR-swizzled per row so that every
-// read is free of bank conflicts: K chunk j of row r sits at slot j ^ sk(r),
-// V chunk j at j ^ sv(r).
+// issuing wave for about 100 cycles.)  K operands are read with one
+// ds_read_b128 per lane (the LDS serves 16 lanes of a b128 read per cycle;
+// a pair of ds_read_b64 was measured to conflict two ways, because a b64
+// read is served 32 lanes at a time and lanes l and l + 16 then share
+// banks), V^T operands with ds_read_b64_tr_b16, which hands each lane one d
+// column of four key rows (lanes 4e..4e+3 of a 16-lane group address row e,
+// lane i receives element i of each row).  16-byte chunks are XOR-swizzled
+// per row so that every read is free of bank conflicts: K chunk j of row r
+// sits at slot j ^ sk(r), V chunk j at j ^ sv(r).
 //
-// Lazy rescaling: the exponent reference m is raised only when a tile's row
-// max exceeds it by more than 8 / (scale log2 e), i.e. when a weight would
-// exceed 2^8; otherwise the old reference is kept and the rescale factor is
-// exactly 1.  The result is unchanged in exact arithmetic (any reference
-// cancels in O / l) and the weights stay <= 256, far from fp32 overflow.
+// Lazy rescaling: the exponent reference is a past row max, and a tile is
+// first weighted against it without computing its own row max.  The tile is
+// kept if no lane's weights sum above 2^8; only otherwise is the row max
+// taken and the reference raised to it (O and l scaled by exp2(old - new)).
+// The result is unchanged in exact arithmetic (any reference cancels in
+// O / l), the weights stay <= 256, far from fp32 overflow, and most tiles
+// skip both the row max and the rescale.
 //
 // Masking: keys at or past the sequence end score -inf (the pages fill
 // padded key rows with zeros, which would give them score 0; the definition
@@ -80,11 +84,7 @@ namespace {
 #ifndef FA_LOOKAHEAD
 #define FA_LOOKAHEAD 3
 #endif
-// K/V staging: 0 = global loads of tile t + 2 issued in M(t), written to LDS
-// in V(t); 1 = loads of tile t + 1 issued in V(t - 1), written in M(t).
-#ifndef FA_STORE_IN_M
-#define FA_STORE_IN_M 0
-#endif
+
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;  // 512
@@ -134,10 +134,10 @@ __device__ __forceinline__ void static_for(F &&f) {
 // awaited with lgkm_wait, which is tied to the destination registers so no
 // consumer can be scheduled above it.
 template <int OFF>
-__device__ __forceinline__ u32x2_t lds_read_b64(uint32_t addr) {
+__device__ __forceinline__ u32x4_t lds_read_b128(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset");
-  u32x2_t d;
-  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
+  u32x4_t d;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
   return d;
 }
 template <int OFF>
@@ -148,8 +148,12 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
   return d;
 }
 template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x2_t &a, u32x2_t &b, u32x2_t &c, u32x2_t &d) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+__device__ __forceinline__ void lgkm_wait(u32x4_t &a, u32x2_t &b, u32x2_t &c) {
+  asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4_t &a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
 }
 template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x2_t &a, u32x2_t &b) {
@@ -258,16 +262,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     d_pk[i] = d_ck[i] + (long long)row * rs;
     d_pv[i] = d_cv[i] + (long long)row * rs;
   }
-  u32x4_t stg[2 * C::DPW];  // this wave's slots of the tile in flight: K then V
-  auto load_tile = [&](int t_) {
+  constexpr int NLD = 2 * C::DPW;  // loads per wave per tile: K slots, then V slots
+  u32x4_t stg[NLD];                // this wave's slots of the tile in flight
+  const uint16_t *src[NLD];        // their sources in the tile being loaded
+  auto prep_tile = [&](int t_) {
     const int t = __builtin_amdgcn_readfirstlane(t_);
     const int key0 = t * kBN;
     if (key0 + kBN <= n) {  // whole tile in range: one 64-bit add per load
       const long long off = (long long)key0 * rs;
 #pragma unroll
       for (int i = 0; i < C::DPW; ++i) {
-        stg[i] = *reinterpret_cast<const u32x4_t *>(d_pk[i] + off);
-        stg[C::DPW + i] = *reinterpret_cast<const u32x4_t *>(d_pv[i] + off);
+        src[i] = d_pk[i] + off;
+        src[C::DPW + i] = d_pv[i] + off;
       }
     } else {  // ragged last tile: rows past the end read row n - 1 (masked later)
 #pragma unroll
@@ -275,10 +281,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
         int key = key0 + d_row[i];
         key = key < n ? key : n - 1;
         const long long ro = (long long)key * rs;
-        stg[i] = *reinterpret_cast<const u32x4_t *>(d_ck[i] + ro);
-        stg[C::DPW + i] = *reinterpret_cast<const u32x4_t *>(d_cv[i] + ro);
+        src[i] = d_ck[i] + ro;
+        src[C::DPW + i] = d_cv[i] + ro;
       }
     }
+  };
+  auto load_tile = [&](int t) {
+    prep_tile(t);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) stg[j] = *reinterpret_cast<const u32x4_t *>(src[j]);
   };
   auto store_tile = [&](int t_) {
     const int t = __builtin_amdgcn_readfirstlane(t_);
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS char *)smem));
 
   // ---- running state ------------------------------------------------------
-  float m_ref = neg_inf();  // exponent reference (raw score units)
+  float mbl = neg_inf();    // exponent reference, exp2 domain
   float l_run = 0.f;        // this lane's partial row sum (its half of the keys)
   f32x16_t o[D / 32];
 #pragma unroll
@@ -321,7 +332,6 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   f32x16_t sc[2];
   bf16x8_t pb[kBN / 16];
   const float sl2 = a.scale_log2;
-  const float lazy_thr = a.lazy_thr;
 
   // M(t): S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T, interleaved.  Step i
   // does S product (kb = i % 2, c = i / 2) and P.V product (db = i / 4,
@@ -331,19 +341,19 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   constexpr int NB = kLook + 1;
   auto m_body = [&](auto do_s, auto do_pv, uint32_t kbase, uint32_t vbase) {
     constexpr bool S = decltype(do_s)::value, PV = decltype(do_pv)::value;
-    constexpr int RPS = (S ? 2 : 0) + (PV ? 2 : 0);  // LDS reads per step
+    constexpr int RPS = (S ? 1 : 0) + (PV ? 2 : 0);  // LDS reads per step
     uint32_t ka[D / 16], va[D / 32];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) ka[c] = kbase + kofs[c];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) va[db] = vbase + vofs[db];
-    u32x2_t kr[NB][2], vr[NB][2];
+    u32x4_t kr[NB];
+    u32x2_t vr[NB][2];
     auto issue = [&](auto I) {
       constexpr int i = decltype(I)::value, b = i % NB;
       if constexpr (S) {
         constexpr int kbk = i & 1, c = i >> 1;
-        kr[b][0] = lds_read_b64<kbk * 32 * C::ROWB>(ka[c]);
-        kr[b][1] = lds_read_b64<kbk * 32 * C::ROWB + 8>(ka[c]);
+        kr[b] = lds_read_b128<kbk * 32 * C::ROWB>(ka[c]);
       }
       if constexpr (PV) {
         constexpr int db = i >> 2, c = i & 3;
@@ -357,14 +367,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       if constexpr (i + kLook < NSTEP) issue(std::integral_constant<int, i + kLook>{});
       constexpr int ahead = (NSTEP - 1 - i) < kLook ? (NSTEP - 1 - i) : kLook;
       if constexpr (S && PV)
-        lgkm_wait<RPS * ahead>(kr[b][0], kr[b][1], vr[b][0], vr[b][1]);
+        lgkm_wait<RPS * ahead>(kr[b], vr[b][0], vr[b][1]);
       else if constexpr (S)
-        lgkm_wait<RPS * ahead>(kr[b][0], kr[b][1]);
+        lgkm_wait<RPS * ahead>(kr[b]);
       else
         lgkm_wait<RPS * ahead>(vr[b][0], vr[b][1]);
       if constexpr (S) {
         constexpr int kbk = i & 1, c = i >> 1;
-        sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_bf16(kr[b][0], kr[b][1]), q[c],
+        sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[b]), q[c],
                                                           c == 0 ? f32x16_t{} : sc[kbk], 0, 0, 0);
       }
       if constexpr (PV) {
@@ -380,11 +390,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   auto m_phase = [&](int t) {
     const bool do_s = t < Tw;
     const bool do_pv = t >= 1 && t <= Tw;
-#if FA_STORE_IN_M
-    if (t >= 1 && t + 1 < T) store_tile(t + 1);
-#else
     if (t + 2 < T) load_tile(t + 2);
-#endif
     if (!do_s && !do_pv) return;
     const uint32_t kbase = lds_base + (t & (kStages - 1)) * C::STAGE;
     const uint32_t vbase = lds_base + ((t - 1) & (kStages - 1)) * C::STAGE;
@@ -401,14 +407,42 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   // V(t): softmax update of S_t -> P_t (bf16), l, rescaled O.
   // V(t) also writes this wave's share of tile t + 2 (loaded during M(t)) into
   // its LDS stage, whose previous tile t - 2 was last read two phases earlier.
+  //
+  // The reference is kept in the exp2 domain (mbl = scale log2(e) times a
+  // past row max).  Every tile is first tried against the current reference
+  // (fast path: no row max at all); it is accepted when no lane's weights sum
+  // above 2^8, so every weight stays <= 2^8.  Otherwise (scores outgrew the
+  // reference, or no reference yet) the row max is taken and the reference
+  // rebased on it, with O and l rescaled by exp2(old - new).
+  auto weights = [&](float d) {  // P = exp2(x - d) into pb; returns this lane's sum
+    float pq[4];
+#pragma unroll
+    for (int c = 0; c < kBN / 16; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = exp2_fast(sc[c >> 1][8 * (c & 1) + e] - d);
+        const float p1 = exp2_fast(sc[c >> 1][8 * (c & 1) + e + 1] - d);
+        pb[c][e] = (__bf16)p0;
+        pb[c][e + 1] = (__bf16)p1;
+        const int j = (c & 1) + 2 * (e >> 2);  // four partial sums: short add chains
+        if (c < 2 && (e & 3) == 0)
+          pq[j] = p0 + p1;
+        else
+          pq[j] += p0 + p1;
+      }
+    return (pq[0] + pq[1]) + (pq[2] + pq[3]);
+  };
   auto v_phase = [&](int t) {
-#if FA_STORE_IN_M
-    if (t + 2 < T) load_tile(t + 2);
-#else
     if (t + 2 < T) store_tile(t + 2);
-#endif
     if (t >= Tw) return;
     const int key0 = t * kBN;
+    const float g = (mbl == neg_inf()) ? 0.f : mbl;  // ghost-row guard
+    // x = S scale log2(e) - g; keys past the end and (causal) after the query
+    // are -inf
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[b][r] = __builtin_fmaf(sc[b][r], sl2, -g);
     if ((key0 + kBN > n) || (CAUSAL && key0 + kBN - 1 > qw0)) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
@@ -418,44 +452,38 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
           if (!(key < n && (!CAUSAL || key <= qrow))) sc[b][r] = neg_inf();
         }
     }
-    // row max: four independent max3 chains over 8 scores each, then combined
-    float mq[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int b = j >> 1, r0 = 8 * (j & 1);
-      float m = max3f(sc[b][r0], sc[b][r0 + 1], sc[b][r0 + 2]);
-      m = max3f(m, sc[b][r0 + 3], sc[b][r0 + 4]);
-      m = max3f(m, sc[b][r0 + 5], sc[b][r0 + 6]);
-      mq[j] = max2f(m, sc[b][r0 + 7]);
+    float ps = 0.f, alpha = 1.f;
+    bool slow = __builtin_amdgcn_ballot_w64(mbl == neg_inf()) != 0;
+    if (!slow) {
+      ps = weights(0.f);
+      slow = __builtin_amdgcn_ballot_w64(!(ps <= 256.f)) != 0;  // NaN / inf fail too
     }
-    float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
-    mx = pair_max(mx);
-    const bool bump = mx > m_ref + lazy_thr;  // also true on the first finite tile
-    float alpha = 1.f;
-    if (bump) {
-      alpha = exp2_fast((m_ref - mx) * sl2);  // 0 when m_ref = -inf
-      m_ref = mx;
-    }
-    const float mb = (m_ref == neg_inf() ? 0.f : m_ref) * sl2;  // ghost-row guard
-    float pq[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums (short add chains)
+    if (slow) {
+      // row max of x: four independent max3 chains over 8 values, then combined
+      float mq[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(__builtin_fmaf(sc[b][r], sl2, -mb));
-        sc[b][r] = p;
-        pq[(r & 1) + 2 * b] += p;
+      for (int j = 0; j < 4; ++j) {
+        const int b = j >> 1, r0 = 8 * (j & 1);
+        float m = max3f(sc[b][r0], sc[b][r0 + 1], sc[b][r0 + 2]);
+        m = max3f(m, sc[b][r0 + 3], sc[b][r0 + 4]);
+        m = max3f(m, sc[b][r0 + 5], sc[b][r0 + 6]);
+        mq[j] = max2f(m, sc[b][r0 + 7]);
       }
-    const float ps = (pq[0] + pq[1]) + (pq[2] + pq[3]);
-    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
+      mx = pair_max(mx);
+      // rebase when the row grew past the reference, or on its first finite score
+      const bool bump = (mbl == neg_inf()) ? (mx > neg_inf()) : (mx > 0.f);
+      const float delta = bump ? mx : 0.f;
+      if (bump) {
+        const float mbl_new = g + mx;
+        alpha = exp2_fast(mbl - mbl_new);  // 0 when there was no reference
+        mbl = mbl_new;
+      }
+      ps = weights(delta);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
     l_run = l_run * alpha + ps;
-#pragma unroll
-    for (int c = 0; c < kBN / 16; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[c][e] = (__bf16)sc[c >> 1][8 * (c & 1) + e];
   };
 
   // ---- prologue: tiles 0 and 1 in LDS ---------------------------------------
@@ -492,10 +520,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
                             (__bf16)(o[db][4 * gq + 2] * inv), (__bf16)(o[db][4 * gq + 3] * inv)};
         *reinterpret_cast<bf16x4_t *>(orow + 32 * db + 8 * gq + 4 * h) = x;
       }
-    if (a.lse != nullptr && h == 0) {
-      const float m_fin = (m_ref == neg_inf()) ? 0.f : m_ref;
+    if (a.lse != nullptr && h == 0) {  // lse = ln 2 (mbl + log2 l)
+      const float m_fin = (mbl == neg_inf()) ? 0.f : mbl;
       a.lse[tc.lbase + (long long)qrow * a.lse_row_stride] =
-          l_tot > 0.f ? m_fin * a.scale + __logf(l_tot) : neg_inf();
+          l_tot > 0.f ? (m_fin + __log2f(l_tot)) * 0.693147180559945309f : neg_inf();
     }
   }
 }
@@ -524,7 +552,6 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   const long long grid = (long long)a.batch * a.H * a.n_qtiles;
   if (grid > 0x7fffffffll || grid <= 0) return hipErrorInvalidValue;
   a.grid = (int)grid;
-  a.lazy_thr = 8.0f / a.scale_log2;  // weights stay <= 2^8 between rescales
   if (d == 64) return launch_d<64>(a, causal, varlen, stream);
   if (d == 128) return launch_d<128>(a, causal, varlen, stream);
   return hipErrorInvalidValue;

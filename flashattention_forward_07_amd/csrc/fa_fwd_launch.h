@@ -34,7 +34,6 @@ struct FwdArgs {
   int grid;      // workgroups launched                -- set by the launcher
   float scale;       // softmax scale applied to q.k
   float scale_log2;  // scale * log2(e), for exp2
-  float lazy_thr;    // raw-score slack of the exponent reference (bf16 kernel)
 };
 
 // Smallest number of query rows any kernel gives one workgroup (used by the
