@@ -82,7 +82,12 @@ namespace {
 #define FA_PRIO_V 0
 #endif
 #ifndef FA_LOOKAHEAD
-#define FA_LOOKAHEAD 3
+#define FA_LOOKAHEAD 4
+#endif
+// Where a wave issues the global loads of its staging slots: 0 = start of
+// M(t), tile t + 2; 1 = end of V(t), tile t + 3.
+#ifndef FA_LOAD_AT
+#define FA_LOAD_AT 0
 #endif
 
 
@@ -111,9 +116,13 @@ struct Bf16Tile {
   }
 };
 
-// Workgroup barrier that also completes this wave's LDS writes first.
+// Workgroup barrier that also completes this wave's LDS writes first.  The
+// wait is the builtin (lgkmcnt = 0, other counters untouched) rather than
+// inline assembly, so the compiler's own wait insertion knows that scalar
+// loads issued before it have completed and does not wait again inside the
+// loop, where such a wait would also stall on this wave's LDS writes.
 __device__ __forceinline__ void wg_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -246,21 +255,26 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   }
 
   // ---- K/V tile staging: global -> registers -> LDS ---------------------
-  // A tile is 2 * TILE bytes of LDS, 16-byte slots; slot p holds row p / CPR.
-  // Wave wv owns slots (wv * DPW + i) * 64 + lane: it loads them into
-  // registers in its M(t) phase and writes them in its next M phase.
+  // A tile is 2 * TILE bytes of LDS in 16-byte slots.  Wave wv moves chunks
+  // p = (wv * DPW + i) * 64 + lane, i.e. row p / CPR, chunk p % CPR: the
+  // global loads read each row's chunks in order (consecutive lanes,
+  // consecutive addresses, which the address unit takes fastest) and the LDS
+  // writes put chunk j of row r at its swizzled slot.
   int d_row[C::DPW];
-  const uint16_t *d_pk[C::DPW], *d_pv[C::DPW];  // source of the slot in tile 0
+  const uint16_t *d_pk[C::DPW], *d_pv[C::DPW];  // source of the chunk in tile 0
   const uint16_t *d_ck[C::DPW], *d_cv[C::DPW];  // its column in row 0 (ragged path)
+  uint32_t d_lk[C::DPW], d_lv[C::DPW];          // its LDS offsets within a stage
 #pragma unroll
   for (int i = 0; i < C::DPW; ++i) {
     const int p = (wv * C::DPW + i) * kWave + lane;
-    const int row = p / C::CPR, slot = p % C::CPR;
+    const int row = p / C::CPR, chunk = p % C::CPR;
     d_row[i] = row;
-    d_ck[i] = kb + 8 * (slot ^ C::swz_k(row));
-    d_cv[i] = vb + 8 * (slot ^ C::swz_v(row));
+    d_ck[i] = kb + 8 * chunk;
+    d_cv[i] = vb + 8 * chunk;
     d_pk[i] = d_ck[i] + (long long)row * rs;
     d_pv[i] = d_cv[i] + (long long)row * rs;
+    d_lk[i] = row * C::ROWB + 16 * (chunk ^ C::swz_k(row));
+    d_lv[i] = C::TILE + row * C::ROWB + 16 * (chunk ^ C::swz_v(row));
   }
   constexpr int NLD = 2 * C::DPW;  // loads per wave per tile: K slots, then V slots
   u32x4_t stg[NLD];                // this wave's slots of the tile in flight
@@ -293,11 +307,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   };
   auto store_tile = [&](int t_) {
     const int t = __builtin_amdgcn_readfirstlane(t_);
-    char *st = smem + (t & (kStages - 1)) * C::STAGE + (wv * C::DPW) * 1024 + lane * 16;
+    char *st = smem + (t & (kStages - 1)) * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::DPW; ++i) {
-      *reinterpret_cast<u32x4_t *>(st + i * 1024) = stg[i];
-      *reinterpret_cast<u32x4_t *>(st + C::TILE + i * 1024) = stg[C::DPW + i];
+      *reinterpret_cast<u32x4_t *>(st + d_lk[i]) = stg[i];
+      *reinterpret_cast<u32x4_t *>(st + d_lv[i]) = stg[C::DPW + i];
     }
   };
 
@@ -390,7 +404,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   auto m_phase = [&](int t) {
     const bool do_s = t < Tw;
     const bool do_pv = t >= 1 && t <= Tw;
+#if FA_LOAD_AT == 0
     if (t + 2 < T) load_tile(t + 2);
+#endif
     if (!do_s && !do_pv) return;
     const uint32_t kbase = lds_base + (t & (kStages - 1)) * C::STAGE;
     const uint32_t vbase = lds_base + ((t - 1) & (kStages - 1)) * C::STAGE;
@@ -432,9 +448,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       }
     return (pq[0] + pq[1]) + (pq[2] + pq[3]);
   };
-  auto v_phase = [&](int t) {
-    if (t + 2 < T) store_tile(t + 2);
-    if (t >= Tw) return;
+  auto v_softmax = [&](int t) {
     const int key0 = t * kBN;
     const float g = (mbl == neg_inf()) ? 0.f : mbl;  // ghost-row guard
     // x = S scale log2(e) - g; keys past the end and (causal) after the query
@@ -485,14 +499,37 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     }
     l_run = l_run * alpha + ps;
   };
+  auto v_phase = [&](int t) {
+    if (t + 2 < T) store_tile(t + 2);
+    if (t < Tw) v_softmax(t);
+#if FA_LOAD_AT == 1
+    if (t + 3 < T) load_tile(t + 3);
+#endif
+  };
 
-  // ---- prologue: tiles 0 and 1 in LDS ---------------------------------------
+  // ---- prologue: tiles 0 and 1 in LDS (both in flight at once) -------------
   load_tile(0);
-  store_tile(0);
   if (T > 1) {
+    u32x4_t stg0[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) stg0[j] = stg[j];
     load_tile(1);
+    u32x4_t stg1[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      stg1[j] = stg[j];
+      stg[j] = stg0[j];
+    }
+    store_tile(0);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) stg[j] = stg1[j];
     store_tile(1);
+  } else {
+    store_tile(0);
   }
+#if FA_LOAD_AT != 0
+  if (T > 2) load_tile(2);
+#endif
   wg_barrier();
 
   // ---- ping-pong loop: phase ph; group g runs step ph - g ------------------
