@@ -110,15 +110,21 @@ def cpu_baseline(w, inp, budget_s):
                 break
         sample = f"{heads} whole (sequence, head) slices, longest sequences first"
     else:
+        # whole (batch, head) slices in order; a workload that finishes in
+        # under two seconds is repeated so the rate is not timer noise
         B, H = w.B, w.H
-        for i in range(B * H):
-            b, h = divmod(i, H)
+        i = 0
+        while True:
+            b, h = divmod(i % (B * H), H)
             oracle.attention(inp.q[b, h], inp.k[b, h], inp.v[b, h], w.scale, w.causal)
             flops += attention_flops([w.N], 1, w.d, w.causal)
             heads += 1
-            if time.perf_counter() - t0 > budget_s:
+            i += 1
+            el = time.perf_counter() - t0
+            if el > budget_s or (i >= B * H and el > 2.0):
                 break
-        sample = f"{heads} of {B * H} whole (batch, head) slices"
+        sample = (f"{heads} of {B * H} whole (batch, head) slices" if heads <= B * H else
+                  f"the whole workload ({B * H} (batch, head) slices) {heads / (B * H):.0f} times")
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{sample}; {flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
