@@ -139,6 +139,9 @@ def main():
                     choices=[w.name for w in fa_inputs.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--via-op", action="store_true",
+                    help="time the step through the PyTorch operator torch.ops.fa355.fwd "
+                         "(fixed-length workloads; outputs allocated per call)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 1 GiB device copy (for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -183,8 +186,14 @@ def main():
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
         lengths = [w.N] * w.B
 
-        def step():
-            fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, code)
+        if args.via_op:
+            import flashattention_forward_07_amd.torch_ops  # noqa: F401  (registers the op)
+
+            def step():
+                torch.ops.fa355.fwd(q, k, v, w.causal, w.scale)
+        else:
+            def step():
+                fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, code)
         total_tokens = w.B * w.N
 
     flops = attention_flops(lengths, w.H, w.d, w.causal)
@@ -241,7 +250,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B if not w.varlen else int(len(lengths)),
+        "config": {"workload": w.name, "via": "torch.ops.fa355.fwd" if args.via_op else "fa_fwd",
+                   "B": w.B if not w.varlen else int(len(lengths)),
                    "H": w.H, "N": w.N if not w.varlen else int(max(lengths)), "d": w.d,
                    "causal": w.causal, "varlen": w.varlen, "tokens": total_tokens,
                    "flops_per_step": flops},
