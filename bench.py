@@ -59,6 +59,15 @@ def algorithmic_bytes(total_tokens, H, d, elem):
     return total_tokens * H * (4 * d * elem + 4)
 
 
+def naive_bytes(N, B, H, d, elem, causal):
+    """HBM bytes the unfused three-step method cannot avoid per launch: Q, K,
+    V read and O, lse written once, and every allowed score written as fp32,
+    read back, its probability written in the input dtype and read again
+    (N^2 scores per head, about half of them when causal)."""
+    scores = N * (N + 1) / 2 if causal else float(N) * N
+    return B * H * (N * (4 * d * elem + 4) + scores * (4 + 4 + 2 * elem))
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -139,6 +148,9 @@ def main():
                     choices=[w.name for w in fa_inputs.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--method", choices=["fused", "naive"], default="fused",
+                    help="fused: fa_fwd (the library's kernel); naive: fa_naive_fwd, the "
+                         "unfused three-step baseline (fixed-length workloads)")
     ap.add_argument("--via-op", action="store_true",
                     help="time the step through the PyTorch operator torch.ops.fa355.fwd "
                          "(fixed-length workloads; outputs allocated per call)")
@@ -186,7 +198,15 @@ def main():
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
         lengths = [w.N] * w.B
 
-        if args.via_op:
+        if args.method == "naive":
+            ws_bytes = fa.fa_naive_workspace_bytes(w.B, w.H, w.N)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            log(f"[bench] naive three-step method, {ws_bytes / 2**30:.2f} GiB scores workspace")
+
+            def step():
+                fa.fa_naive_fwd(q, k, v, o, lse, ws, ws_bytes, w.B, w.H, w.N, w.d, w.scale,
+                                w.causal, code)
+        elif args.via_op:
             import flashattention_forward_07_amd.torch_ops  # noqa: F401  (registers the op)
 
             def step():
@@ -196,8 +216,12 @@ def main():
                 fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, code)
         total_tokens = w.B * w.N
 
+    if w.varlen and args.method != "fused":
+        raise SystemExit("bench.py: --method naive takes fixed-length workloads")
     flops = attention_flops(lengths, w.H, w.d, w.causal)
     alg_bytes = algorithmic_bytes(total_tokens, w.H, w.d, elem)
+    if args.method == "naive":
+        alg_bytes = naive_bytes(w.N, w.B, w.H, w.d, elem, w.causal)
 
     stream = torch.cuda.current_stream()  # fa_fwd launches on this stream
     for _ in range(args.warmup):
@@ -232,13 +256,15 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
-    traffic = committed_traffic(w.name)
+    traffic = committed_traffic(w.name) if args.method == "fused" else None
     log(f"[bench] {value:.1f} TFLOP/s per step, kernel {achieved:.1f} TFLOP/s = "
         f"{100 * achieved / peak:.1f}% of {peak:.1f}; algorithmic bytes {alg_bytes / 1e6:.1f} MB "
         f"-> {alg_bytes / (kern_ms * 1e-3) / 1e9:.0f} GB/s")
 
     result = {
-        "metric": METRIC if w is fa_inputs.HEADLINE else f"attention fwd TFLOP/s, {w.name}",
+        "metric": (METRIC if w is fa_inputs.HEADLINE and args.method == "fused" else
+                   f"attention fwd TFLOP/s, {w.name}" + ("" if args.method == "fused" else
+                                                       f", {args.method} method")),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -250,7 +276,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "via": "torch.ops.fa355.fwd" if args.via_op else "fa_fwd",
+        "config": {"workload": w.name, "method": args.method,
+                   "via": ("fa_naive_fwd" if args.method == "naive" else
+                           "torch.ops.fa355.fwd" if args.via_op else "fa_fwd"),
                    "B": w.B if not w.varlen else int(len(lengths)),
                    "H": w.H, "N": w.N if not w.varlen else int(max(lengths)), "d": w.d,
                    "causal": w.causal, "varlen": w.varlen, "tokens": total_tokens,
@@ -259,6 +287,12 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
     }
+    if args.method == "naive":
+        # three launches per step, bound by the N x N round trips through HBM
+        gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "traffic": None, "algorithmic_bytes": alg_bytes}
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on the host (~{args.cpu_budget:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)

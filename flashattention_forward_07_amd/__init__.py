@@ -8,6 +8,7 @@ fallback: if ``libfa355.so`` has not been built, loading fails loudly.
 
     o, lse = attention(q, k, v, causal=True)             # [B, H, N, d]
     o, lse = attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=True)
+    o, lse = naive_attention(q, k, v, causal=True)       # unfused baseline
 """
 from __future__ import annotations
 
@@ -18,7 +19,8 @@ import os
 __all__ = [
     "FA_DTYPE_F32", "FA_DTYPE_BF16", "FAError", "fa_fwd", "fa_fwd_varlen",
     "fa_status_string", "fa_last_hip_error", "fa_version", "attention",
-    "attention_varlen", "library_path", "load",
+    "attention_varlen", "library_path", "load", "fa_naive_fwd", "fa_naive_workspace_bytes",
+    "naive_attention",
 ]
 
 FA_DTYPE_F32 = 0
@@ -59,6 +61,11 @@ def load():
     lib.fa_fwd.restype = i32
     lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
     lib.fa_fwd_varlen.restype = i32
+    lib.fa_naive_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, i32, i32, i32, i32, f32,
+                                 i32, i32, P]
+    lib.fa_naive_fwd.restype = i32
+    lib.fa_naive_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.fa_naive_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -106,6 +113,21 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, H, d, scale, ca
                               float(scale), int(bool(causal)), int(dtype), _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_varlen")
+
+
+def fa_naive_workspace_bytes(B, H, N) -> int:
+    """Workspace bytes fa_naive_fwd needs (0 for sizes out of range)."""
+    return int(load().fa_naive_workspace_bytes(int(B), int(H), int(N)))
+
+
+def fa_naive_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal, dtype,
+                 stream=None) -> None:
+    """Enqueue the unfused three-step forward (scores in the workspace)."""
+    st = load().fa_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                             int(workspace_bytes), int(B), int(H), int(N), int(d), float(scale),
+                             int(bool(causal)), int(dtype), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_naive_fwd")
 
 
 def fa_status_string(status: int) -> str:
@@ -162,4 +184,25 @@ def attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None,
     lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if with_lse else None
     fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, cu_seqlens.numel() - 1, max_seqlen, H, d,
                   scale, causal, _dtype_code(q), stream)
+    return o, lse
+
+
+def naive_attention(q, k, v, causal=False, scale=None, with_lse=True, workspace=None,
+                    stream=None):
+    """The unfused three-step forward for q, k, v [B, H, N, d]; allocates the
+    N x N workspace with torch unless one (uint8, large enough) is given."""
+    import torch
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for t in (q, k, v):
+        if tuple(t.shape) != (B, H, N, d) or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous tensors of one [B, H, N, d] shape")
+    need = fa_naive_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if with_lse else None
+    fa_naive_fwd(q, k, v, o, lse, workspace, workspace.numel() * workspace.element_size(), B, H,
+                 N, d, scale, causal, _dtype_code(q), stream)
     return o, lse

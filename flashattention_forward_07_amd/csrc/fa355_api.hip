@@ -9,6 +9,7 @@
 
 #include "fa355.h"
 #include "fa_fwd_launch.h"
+#include "fa_naive_launch.h"
 
 namespace {
 
@@ -141,6 +142,67 @@ FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, f
   return launch(a, dtype, d, causal, true, stream);
 }
 
+// Bytes of the scores workspace of fa_naive_fwd: B H N rows of N floats,
+// each row padded to a multiple of 4 floats; 0 for sizes out of range.
+static size_t naive_bytes(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  const long long ld = ((long long)N + 3) & ~3ll;
+  const long long bh = (long long)B * H;
+  if (bh > 65535 || N > (1 << 22)) return 0;
+  const unsigned long long rows = (unsigned long long)bh * N;
+  if (rows > (1ull << 40) / (unsigned long long)ld) return 0;
+  return (size_t)(rows * (unsigned long long)ld * 4ull);
+}
+
+FA_API size_t fa_naive_workspace_bytes(int B, int H, int N) { return naive_bytes(B, H, N); }
+
+FA_API int fa_naive_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                        void *workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                        float scale, int causal, int dtype, void *stream) {
+  int st = value_checks(d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  const size_t need = naive_bytes(B, H, N);
+  if (need == 0) return FA_ERR_SHAPE;
+  st = pointer_checks(q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  if (!workspace) return FA_ERR_NULL;
+  if (misaligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const long long rows = (long long)B * H * N;
+  const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  const size_t tbytes = (size_t)rows * d * esz, lbytes = (size_t)rows * sizeof(float);
+  if (overlap(o, tbytes, q, tbytes) || overlap(o, tbytes, k, tbytes) ||
+      overlap(o, tbytes, v, tbytes))
+    return FA_ERR_ALIAS;
+  if (lse && (overlap(lse, lbytes, q, tbytes) || overlap(lse, lbytes, k, tbytes) ||
+              overlap(lse, lbytes, v, tbytes) || overlap(lse, lbytes, o, tbytes)))
+    return FA_ERR_ALIAS;
+  if (overlap(workspace, need, q, tbytes) || overlap(workspace, need, k, tbytes) ||
+      overlap(workspace, need, v, tbytes) || overlap(workspace, need, o, tbytes) ||
+      (lse && overlap(workspace, need, lse, lbytes)))
+    return FA_ERR_ALIAS;
+  fa355::NaiveArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.s = static_cast<float *>(workspace);
+  a.n = N;
+  a.ld = (N + 3) & ~3;
+  a.bh = B * H;
+  a.scale = scale;
+  const hipError_t e = fa355::launch_naive(a, dtype, d, causal != 0,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 FA_API const char *fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
@@ -152,6 +214,7 @@ FA_API const char *fa_status_string(int status) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors need 16-byte alignment, lse 4-byte";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed (see fa_last_hip_error)";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than fa_naive_workspace_bytes";
     default: return "unknown status";
   }
 }

@@ -19,12 +19,12 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing, frees nothing, keeps no workspace and
- *     never synchronises.
+ *     library allocates nothing, frees nothing and never synchronises; only
+ *     fa_naive_fwd uses a workspace, which the caller provides.
  *   - A call validates its arguments on the host; on any error it returns a
  *     nonzero FA_ERR_* code and enqueues nothing.  On success it enqueues
- *     one kernel on `stream` (a hipStream_t passed as void*; NULL = the null
- *     stream) and returns FA_OK at once.  Faults inside the kernel surface
+ *     its kernel(s) on `stream` (a hipStream_t passed as void*; NULL = the
+ *     null stream) and returns FA_OK at once.  Faults inside the kernel surface
  *     at the caller's next synchronisation, as usual for HIP.
  *   - q, k, v and o share one element type, `dtype`: FA_DTYPE_BF16
  *     (bfloat16 storage; products and sums in fp32, the softmax weights
@@ -39,6 +39,8 @@
  */
 #ifndef FA355_H
 #define FA355_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -60,6 +62,7 @@ extern "C" {
 #define FA_ERR_ALIGN 6    /* a tensor pointer is misaligned */
 #define FA_ERR_ALIAS 7    /* an output overlaps an input or the other output */
 #define FA_ERR_HIP 8      /* the HIP launch failed; see fa_last_hip_error() */
+#define FA_ERR_WORKSPACE 9 /* workspace smaller than fa_naive_workspace_bytes() */
 
 /*
  * fa_fwd -- attention forward over a fixed-length batch.
@@ -103,6 +106,38 @@ FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o,
                          float *lse, const int *cu_seqlens, int nseq,
                          int max_seqlen, int H, int d, float scale,
                          int causal, int dtype, void *stream);
+
+/*
+ * fa_naive_fwd -- the same attention forward computed the unfused way the
+ * pages start from ("How Did I Write My First FlashAttention Kernel in
+ * CUDA?", standard attention and its three passes of softmax; "Mini
+ * FlashAttention", section 2 on why fusing matters): three kernels,
+ *     1. S = Q K^T * scale into the workspace (fp32, N x N per (b, h)),
+ *     2. per row: max, sum of exp, P = exp(S - max) / sum written over the
+ *        row in dtype, lse = max + ln(sum),
+ *     3. O = P V.
+ * It exists as the baseline the fused kernel is measured against; its
+ * results agree with fa_fwd to the dtype's rounding (not bit for bit).
+ *
+ *   q, k, v, o, lse, B, H, N, d, scale, causal, dtype  as for fa_fwd
+ *   workspace        DEVICE buffer, 16-byte aligned, at least
+ *                    fa_naive_workspace_bytes(B, H, N) bytes, owned by the
+ *                    caller; its contents are overwritten and must not
+ *                    overlap any tensor argument.
+ *   workspace_bytes  its size (FA_ERR_WORKSPACE when too small)
+ *
+ * B H must not exceed 65535 and N not 2^22 (FA_ERR_SHAPE).  Causal score
+ * tiles entirely above the diagonal are not computed.
+ */
+FA_API int fa_naive_fwd(const void *q, const void *k, const void *v, void *o,
+                        float *lse, void *workspace, size_t workspace_bytes,
+                        int B, int H, int N, int d, float scale, int causal,
+                        int dtype, void *stream);
+
+/* Workspace bytes fa_naive_fwd needs: B H N rows of N floats, each row
+ * rounded up to a multiple of 4 floats; 0 if a size is <= 0 or out of the
+ * range fa_naive_fwd accepts. */
+FA_API size_t fa_naive_workspace_bytes(int B, int H, int N);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 FA_API const char *fa_status_string(int status);

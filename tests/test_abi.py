@@ -35,7 +35,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert set(_declared()) == {"fa_fwd", "fa_fwd_varlen", "fa_status_string",
+    assert set(_declared()) == {"fa_fwd", "fa_fwd_varlen", "fa_naive_fwd",
+                                "fa_naive_workspace_bytes", "fa_status_string",
                                 "fa_last_hip_error", "fa_version"}
 
 
@@ -112,6 +113,38 @@ def test_varlen_rejects_bad_arguments(lib):
     assert _fwd_varlen(lib, nseq=1 << 20, max_seqlen=1 << 30, H=64) == c["FA_ERR_SHAPE"]
     assert _fwd_varlen(lib, nseq=0) == 0
     assert _fwd_varlen(lib, max_seqlen=0) == 0
+
+
+def _naive(lib, q=A, k=A + 0x1000, v=A + 0x2000, o=A + 0x3000, lse=None, ws=A + 0x10000,
+           ws_bytes=None, B=1, H=1, N=16, d=64, scale=0.125, causal=0, dtype=BF16):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_naive_workspace_bytes(B, H, N)
+    return lib.fa_naive_fwd(q, k, v, o, lse, ws, ws_bytes, B, H, N, d, ctypes.c_float(scale),
+                            causal, dtype, None)
+
+
+def test_naive_workspace_size(lib):
+    # rows of N floats rounded up to a multiple of 4
+    assert lib.fa_naive_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 8 * 4
+    assert lib.fa_naive_workspace_bytes(4, 32, 4096) == 4 * 32 * 4096 * 4096 * 4
+    assert lib.fa_naive_workspace_bytes(1, 1, 1) == 16
+    for bad in ((0, 1, 1), (1, -1, 1), (1, 1, 0), (65536, 1, 8), (1, 1, (1 << 22) + 1)):
+        assert lib.fa_naive_workspace_bytes(*bad) == 0
+
+
+def test_naive_rejects_bad_arguments(lib):
+    c = _status_codes()
+    assert _naive(lib, ws=None) == c["FA_ERR_NULL"]
+    assert _naive(lib, q=None) == c["FA_ERR_NULL"]
+    assert _naive(lib, ws=A + 0x10008) == c["FA_ERR_ALIGN"]
+    assert _naive(lib, ws_bytes=100) == c["FA_ERR_WORKSPACE"]
+    assert _naive(lib, d=32) == c["FA_ERR_HEAD_DIM"]
+    assert _naive(lib, dtype=3) == c["FA_ERR_DTYPE"]
+    assert _naive(lib, scale=-1.0) == c["FA_ERR_SCALE"]
+    assert _naive(lib, B=65536, H=1) == c["FA_ERR_SHAPE"]
+    assert _naive(lib, o=A) == c["FA_ERR_ALIAS"]
+    assert _naive(lib, ws=A + 0x2000) == c["FA_ERR_ALIAS"]  # workspace over v
+    assert _naive(lib, N=0) == 0 and _naive(lib, B=0, ws=None) == 0
 
 
 def test_python_binding_raises_on_error(lib):
