@@ -139,6 +139,56 @@ def cpu_baseline(w, inp, budget_s):
             "sample": f"{sample}; {flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
 
 
+def compare_naive(torch, fa, reps=20, warmup=5):
+    """Fused kernel against the unfused three-step method on the same inputs:
+    one head of d=64 (the single-head shape of the pages' naive-versus-tiled
+    timing) in fp32 and bf16, and 32 heads in bf16, over N = 128 .. 16384,
+    non-causal.  Per point: mean launch time of each method (HIP events on the
+    launch stream), the speedup, and the largest |O_fused - O_naive|."""
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        st = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    print("| dtype | B x H | N | fused ms | naive ms | naive / fused | max abs O diff |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    for dtype, H, ns in (("f32", 1, [128, 256, 512, 1024, 2048, 4096, 8192, 16384]),
+                         ("bf16", 1, [128, 256, 512, 1024, 2048, 4096, 8192, 16384]),
+                         ("bf16", 32, [128, 512, 1024, 2048, 4096, 8192])):
+        for N in ns:
+            B, d = 1, 64
+            inp = fa_inputs.make_fixed(B, H, N, d, dtype, seed=9000 + N + H)
+            if dtype == "bf16":
+                q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+                           for x in inp.device_arrays())
+                code = fa.FA_DTYPE_BF16
+            else:
+                q, k, v = (torch.from_numpy(x).to("cuda") for x in inp.device_arrays())
+                code = fa.FA_DTYPE_F32
+            scale = float(np.float32(1.0 / math.sqrt(d)))
+            o1, o2 = torch.empty_like(q), torch.empty_like(q)
+            l1 = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+            l2 = torch.empty_like(l1)
+            wsb = fa.fa_naive_workspace_bytes(B, H, N)
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            tf = timed(lambda: fa.fa_fwd(q, k, v, o1, l1, B, H, N, d, scale, False, code))
+            tn = timed(lambda: fa.fa_naive_fwd(q, k, v, o2, l2, ws, wsb, B, H, N, d, scale,
+                                               False, code))
+            diff = (o1.float() - o2.float()).abs().max().item()
+            print(f"| {dtype} | {B} x {H} | {N} | {tf:.4f} | {tn:.4f} | {tn / tf:.2f} | "
+                  f"{diff:.2e} |", flush=True)
+            del ws
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +204,10 @@ def main():
     ap.add_argument("--via-op", action="store_true",
                     help="time the step through the PyTorch operator torch.ops.fa355.fwd "
                          "(fixed-length workloads; outputs allocated per call)")
+    ap.add_argument("--compare-naive", action="store_true",
+                    help="instead of the bench line, time the fused kernel against the naive "
+                         "three-step method over a range of N (one head and 32 heads, d=64, "
+                         "non-causal) and print a markdown table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 1 GiB device copy (for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -169,6 +223,9 @@ def main():
     import flashattention_forward_07_amd as fa
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.compare_naive:
+        compare_naive(torch, fa)
+        return
 
     w = fa_inputs.by_name(args.workload)
     log(f"[bench] workload {w.name}: generating seeded inputs")

@@ -4,9 +4,10 @@
 // Did I Write My First FlashAttention Kernel in CUDA?", the three passes of
 // softmax; "Mini FlashAttention", section 2): per (batch, head)
 //   1. S = scale Q K^T, written to a caller-provided N x N fp32 workspace;
-//   2. each row of S: max, sum of exp, then P = exp(S - max) / sum written
-//      back over the row in the input dtype (bf16 P takes the first half of
-//      the row's bytes), and lse = max + ln(sum);
+//   2. each row of S: its max and sum of exp (one pass, the sum rebased as
+//      the max grows), then P = exp(S - max) / sum written back over the
+//      row in the input dtype (bf16 P takes the first half of the row's
+//      bytes), and lse = max + ln(sum);
 //   3. O = P V.
 // The N x N matrix goes through HBM twice, which is what the fused kernel
 // avoids.  Causal: key j > query i is masked; score tiles entirely above
@@ -29,9 +30,10 @@ constexpr int kNT = 256;  // threads per workgroup (4 waves)
 
 // ---- 1. scores (bf16) ------------------------------------------------------
 // Workgroup: 128 queries x 128 keys of one (b, h); wave w owns queries
-// 32 w .. 32 w + 31 and computes S^T = K Q^T in four 32-key blocks (lane l
-// holds query l % 32, keys 8 (r / 4) + 4 (l / 32) + r % 4 of a block in
-// register r).  Operands come straight from global memory (L2): the K rows
+// 32 w .. 32 w + 31 and computes S = Q K^T in four 32-key blocks (lane l
+// holds key l % 32 and queries 8 (r / 4) + 4 (l / 32) + r % 4 of a block in
+// register r, so each store writes 128 contiguous bytes of a row per
+// half-wave).  Operands come straight from global memory (L2): the K rows
 // and the wave's resident Q rows are 16-byte reads.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kNT) void scores_bf16(NaiveArgs a) {
@@ -44,7 +46,8 @@ __global__ __launch_bounds__(kNT) void scores_bf16(NaiveArgs a) {
   const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q) + (long long)bh * n * D;
   const uint16_t *kb = reinterpret_cast<const uint16_t *>(a.k) + (long long)bh * n * D;
   float *sb = a.s + (long long)bh * n * a.ld;
-  const int qi = q0 + 32 * wv + l32;
+  const int qw = q0 + 32 * wv;  // the wave's first query
+  const int qi = qw + l32;      // query row this lane reads for the A operand
   bf16x8_t qr[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
@@ -52,35 +55,35 @@ __global__ __launch_bounds__(kNT) void scores_bf16(NaiveArgs a) {
     if (qi < n) x = *reinterpret_cast<const u32x4_t *>(qb + (long long)qi * D + 16 * c + 8 * h);
     qr[c] = __builtin_bit_cast(bf16x8_t, x);
   }
-#pragma unroll
-  for (int kb32 = 0; kb32 < 4; ++kb32) {
-    const int kr = k0 + 32 * kb32 + l32;  // key row this lane reads for the A operand
-    f32x16_t acc = {};
+  // K rows of block kb32 + 1 are loaded while block kb32's products run
+  u32x4_t kx[D / 16];
+  auto load_k = [&](int kb32) {
+    const int key = k0 + 32 * kb32 + l32;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (kr < n) x = *reinterpret_cast<const u32x4_t *>(kb + (long long)kr * D + 16 * c + 8 * h);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), qr[c], acc,
-                                                    0, 0, 0);
+      kx[c] = u32x4_t{0u, 0u, 0u, 0u};
+      if (key < n) kx[c] = *reinterpret_cast<const u32x4_t *>(kb + (long long)key * D + 16 * c + 8 * h);
     }
-    if (qi < n) {
-      float *row = sb + (long long)qi * a.ld;
+  };
+  load_k(0);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {  // keys 8 g + 4 h + 0..3: one 16-byte store when in range
-        const int key = k0 + 32 * kb32 + 8 * g + 4 * h;
-        float v[4];
+  for (int kb32 = 0; kb32 < 4; ++kb32) {
+    const int key = k0 + 32 * kb32 + l32;  // key row this lane read, and its output column
+    u32x4_t kc[D / 16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = key + e;
-          v[e] = (CAUSAL && kk > qi) ? neg_inf() : acc[4 * g + e] * a.scale;
-        }
-        if (key + 3 < n) {  // rows are 16-byte aligned (ld % 4 == 0)
-          *reinterpret_cast<f32x4_t *>(row + key) = f32x4_t{v[0], v[1], v[2], v[3]};
-        } else {
+    for (int c = 0; c < D / 16; ++c) kc[c] = kx[c];
+    if (kb32 + 1 < 4) load_k(kb32 + 1);
+    f32x16_t acc = {};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (key + e < n) row[key + e] = v[e];
-        }
+    for (int c = 0; c < D / 16; ++c)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[c], __builtin_bit_cast(bf16x8_t, kc[c]), acc,
+                                                    0, 0, 0);
+    if (key < n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = qw + 8 * (r / 4) + 4 * h + r % 4;
+        if (qrow < n)
+          sb[(long long)qrow * a.ld + key] = (CAUSAL && key > qrow) ? neg_inf() : acc[r] * a.scale;
       }
     }
   }
@@ -107,13 +110,27 @@ __global__ __launch_bounds__(kNT) void scores_f32(NaiveArgs a) {
 }
 
 // ---- 2. row softmax (both dtypes) ------------------------------------------
-// One wave per row: pass 1 max, pass 2 sum of exp, pass 3 P = exp(s - m) / l
-// over the allowed keys, written in the input dtype from the start of the
-// row, with zeros after them up to the last key P.V reads (the end of the
-// causal diagonal's 64-key block, or N; bf16 rounds that up to the 8-key
-// chunk P.V loads).  Pass 3 reads a chunk of 64 lanes x 4 scores before it
-// writes that chunk's P, and P bytes never reach scores not yet read (2
-// bytes per bf16 P sit below 4 bytes per score).
+// One wave per row, two passes over the allowed keys: pass 1 keeps a running
+// max and a sum of exp rebased to it (each lane over its own 4-key chunks,
+// then merged across the wave); pass 2 writes P = exp(s - m) / l in the
+// input dtype from the start of the row, with zeros after the allowed keys up
+// to the last key P.V reads (the end of the causal diagonal's 64-key block,
+// or N; bf16 rounds that up to the 8-key chunk P.V loads).  Pass 2 reads a
+// chunk of 64 lanes x 4 scores before it writes that chunk's P, and P bytes
+// never reach scores not yet read (2 bytes per bf16 P sit below 4 bytes per
+// score).  Rows start 16-byte aligned (ld % 4 == 0), so full chunks are
+// single 16-byte loads.
+__device__ __forceinline__ void load4(const float *s, int j, int len, float (&x)[4]) {
+  if (j + 3 < len) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t *>(s + j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = v[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (j + e < len) ? s[j + e] : neg_inf();
+  }
+}
+
 template <bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(kNT) void softmax_rows(NaiveArgs a) {
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -126,30 +143,45 @@ __global__ __launch_bounds__(kNT) void softmax_rows(NaiveArgs a) {
   int ext = CAUSAL ? ((i / 64 + 1) * 64 < n ? (i / 64 + 1) * 64 : n) : n;
   if (BF16) ext = (ext + 7) & ~7;  // <= 2 ld: inside the row's bytes
   float *s = a.s + row * a.ld;
-  float m = neg_inf();
-  for (int j = lane; j < len; j += 64) m = fmaxf(m, s[j]);
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float l = 0.f;
-  for (int j = lane; j < len; j += 64) l += __expf(s[j] - m);
+  float m = neg_inf(), l = 0.f;
+  for (int j = 4 * lane; j < len; j += 256) {
+    float x[4];
+    load4(s, j, len, x);
+    const float mn = fmaxf(m, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));  // finite: j < len
+    l = l * __expf(m - mn) + (__expf(x[0] - mn) + __expf(x[1] - mn)) +
+        (__expf(x[2] - mn) + __expf(x[3] - mn));
+    m = mn;
+  }
+  float mw = m;
+  for (int off = 32; off > 0; off >>= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
+  l = (l > 0.f) ? l * __expf(m - mw) : 0.f;  // lanes without keys hold m = -inf, l = 0
   for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+  m = mw;
   const float inv = 1.f / l;
-  // chunks of 64 lanes x 4 consecutive keys
   for (int j0 = 0; j0 < ext; j0 += 256) {
     const int j = j0 + 4 * lane;
-    float p[4];
+    float x[4], p[4];
+    load4(s, j, len, x);  // keys past len read as -inf and are never loaded
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = (j + e < len) ? __expf(s[j + e] - m) * inv : 0.f;
-    // (keys past len are never read: j + e < len <= n <= ld)
+    for (int e = 0; e < 4; ++e) p[e] = (j + e < len) ? __expf(x[e] - m) * inv : 0.f;
     __builtin_amdgcn_wave_barrier();  // the whole chunk is read before any of it is written
     if constexpr (BF16) {
       uint16_t *pr = reinterpret_cast<uint16_t *>(s);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j + e < ext) pr[j + e] = __builtin_bit_cast(uint16_t, (__bf16)p[e]);
+      if (j + 3 < ext) {  // ext % 8 == 0 here, so this is every chunk below ext
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)p[0]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[1]) << 16);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)p[2]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)p[3]) << 16);
+        *reinterpret_cast<u32x2_t *>(pr + j) = u32x2_t{lo, hi};  // 8-byte aligned: j % 4 == 0
+      }
     } else {
+      if (j + 3 < ext) {
+        *reinterpret_cast<f32x4_t *>(s + j) = f32x4_t{p[0], p[1], p[2], p[3]};
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j + e < ext) s[j + e] = p[e];
+        for (int e = 0; e < 4; ++e)
+          if (j + e < ext) s[j + e] = p[e];
+      }
     }
   }
   if (a.lse != nullptr && lane == 0) a.lse[row] = m + __logf(l);
@@ -187,23 +219,43 @@ __global__ __launch_bounds__(kNT) void pv_bf16(NaiveArgs a) {
   const uint32_t vbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS uint16_t *)vt));
   const uint32_t vaddr = vbase + 2u * ((8 * (g >> 1) + (j >> 2)) * RS + 16 * (g & 1) + 4 * (j & 3));
   const int wave_keys = CAUSAL ? (q0 + 32 * wv + 32 < n ? q0 + 32 * wv + 32 : n) : n;
+  // the next tile's V chunks and P vectors are loaded into registers while
+  // this tile's products run
+  constexpr int NV = 64 * D / 8 / kNT;  // 16-byte V chunks per thread per tile
+  u32x4_t vx[NV], pn[4];
+  auto load_tile = [&](int t) {
+    const int key0 = 64 * t;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int c = threadIdx.x + u * kNT;
+      const int r = c / (D / 8), col = 8 * (c % (D / 8));
+      vx[u] = u32x4_t{0u, 0u, 0u, 0u};  // rows past n read as zeros
+      if (key0 + r < n) vx[u] = *reinterpret_cast<const u32x4_t *>(vb + (long long)(key0 + r) * D + col);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kk = key0 + 16 * ks + 8 * h;
+      pn[ks] = u32x4_t{0u, 0u, 0u, 0u};
+      if (key0 < wave_keys && kk < n) pn[ks] = *reinterpret_cast<const u32x4_t *>(pr + kk);
+    }
+  };
+  load_tile(0);
   for (int t = 0; t < T; ++t) {
     const int key0 = 64 * t;
-    __syncthreads();
-    // V tile rows key0 .. key0 + 63 (rows past n read as zeros)
-    for (int c = threadIdx.x; c < 64 * D / 8; c += kNT) {
-      const int r = c / (D / 8), col = 8 * (c % (D / 8));
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (key0 + r < n) x = *reinterpret_cast<const u32x4_t *>(vb + (long long)(key0 + r) * D + col);
-      *reinterpret_cast<u32x4_t *>(vt + r * RS + col) = x;
+    __syncthreads();  // every wave is done reading the previous tile
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int c = threadIdx.x + u * kNT;
+      *reinterpret_cast<u32x4_t *>(vt + (c / (D / 8)) * RS + 8 * (c % (D / 8))) = vx[u];
     }
+    u32x4_t pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pb[ks] = pn[ks];
     __syncthreads();
+    if (t + 1 < T) load_tile(t + 1);
     if (key0 >= wave_keys) continue;  // wave-uniform; P is zero there anyway
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {  // 16-key steps
-      const int kk = key0 + 16 * ks + 8 * h;
-      u32x4_t pb = {0u, 0u, 0u, 0u};
-      if (kk < n) pb = *reinterpret_cast<const u32x4_t *>(pr + kk);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const uint32_t ad = vaddr + 2u * (16 * ks * RS + 32 * db);
@@ -213,7 +265,7 @@ __global__ __launch_bounds__(kNT) void pv_bf16(NaiveArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi));
         const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                        __builtin_bit_cast(bf16x8_t, pb), o[db],
+                                                        __builtin_bit_cast(bf16x8_t, pb[ks]), o[db],
                                                         0, 0, 0);
       }
     }
