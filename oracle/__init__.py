@@ -67,11 +67,13 @@ def _bind(lib):
     lib.fa_ref_fwd_varlen_rows.argtypes = [P, P, P, P, i32, i32, i32, f64,
                                            i32, P, i32, P, P]
     lib.fa_ref_online.argtypes = [P, P, P, P, P, i32, i32, f64, i32, i32]
+    lib.fa_ref_fwd_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32,
+                                      f64, i32]
     lib.fa_ref_set_threads.argtypes = [i32]
     lib.fa_ref_set_threads.restype = None
     lib.fa_ref_threads.restype = i32
     for name in ("fa_ref_fwd", "fa_ref_fwd_rows", "fa_ref_fwd_varlen",
-                 "fa_ref_fwd_varlen_rows", "fa_ref_online"):
+                 "fa_ref_fwd_varlen_rows", "fa_ref_online", "fa_ref_fwd_decode"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -130,6 +132,30 @@ def attention_rows(q, k, v, scale, causal, rows):
                                  float(scale), int(bool(causal)), _ptr(rows),
                                  rows.size, _ptr(o), _ptr(lse))
     _check(rc, "fa_ref_fwd_rows")
+    return o, lse
+
+
+def attention_decode(q, k, v, scale, causal=False):
+    """Decode-shaped batch: q [B, H, Nq, d] against k, v [B, H, Nk, d] (or
+    [Nq, d] / [Nk, d] for one head).  The queries are the newest Nq
+    positions of the Nk-long sequence: with the causal mask query i sees
+    keys 0 .. Nk - Nq + i.  Returns (o [.., Nq, d], lse [.., Nq]) float64."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4 or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError("q [B, H, Nq, d] and k, v [B, H, Nk, d] expected")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    o = np.empty((B, H, Nq, d), np.float64)
+    lse = np.empty((B, H, Nq), np.float64)
+    rc = _load().fa_ref_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   B, H, Nq, Nk, d, float(scale), int(bool(causal)))
+    _check(rc, "fa_ref_fwd_decode")
+    if squeeze:
+        return o[0, 0], lse[0, 0]
     return o, lse
 
 

@@ -39,6 +39,7 @@
  * Layouts (strides in elements):
  *   fixed length : q, k, v [B, H, N, d] contiguous; o [B, H, N, d]; lse [B, H, N]
  *   packed varlen: q, k, v [T, H, d] with T = cu_seqlens[nseq]; o [T, H, d]; lse [T, H]
+ *   decode       : q, o [B, H, Nq, d]; k, v [B, H, Nk, d]; lse [B, H, Nq]
  * Return value: 0 on success, -1 on bad arguments, -2 on allocation failure.
  */
 #include <math.h>
@@ -307,6 +308,60 @@ int fa_ref_fwd_varlen_rows(const float *q, const float *k, const float *v,
                            v + base * hs + (long)h * d, hs,
                            allowed_keys(i, n, causal), d, scale, buf,
                            o_rows + (long)t * d, lse_rows + t);
+        }
+        free(buf);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Decode-shaped batch: per (batch, head), Nq queries against Nk keys.
+ * q, o [B, H, Nq, d]; k, v [B, H, Nk, d]; lse [B, H, Nq].  "Mini
+ * FlashAttention", section 1, ties the causal mask to autoregressive decoding
+ * (a token never sees a later one) without fixing the shapes of a decode
+ * step; the reading taken here is that the Nq queries are the newest Nq
+ * positions of an Nk-long sequence.  The mask (key j hidden from query i
+ * when j > i, positions in the whole sequence) then lets query i, 0-based
+ * among the Nq, see keys 0 .. Nk - Nq + i.  Without the mask every query sees all Nk keys.  A query
+ * that sees no key (causal with Nq > Nk) gives O = 0 and lse = -inf. */
+static int visible_keys_decode(int i, int nq, int nk, int causal)
+{
+    long last; /* position of the query in the whole sequence */
+    if (!causal)
+        return nk;
+    last = (long)nk - nq + i;
+    if (last < 0)
+        return 0;
+    return last + 1 < nk ? (int)(last + 1) : nk;
+}
+
+int fa_ref_fwd_decode(const float *q, const float *k, const float *v,
+                      double *o, double *lse, int B, int H, int Nq, int Nk,
+                      int d, double scale, int causal)
+{
+    long nrows, r;
+    int bad = 0;
+
+    if (!q || !k || !v || !o || !lse || B < 0 || H < 0 || Nq < 0 || Nk < 0 ||
+        d <= 0)
+        return -1;
+    nrows = (long)B * H * Nq;
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * (Nk > 0 ? Nk : 1));
+        if (!buf) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (r = 0; r < nrows; ++r) {
+            long bh = r / (Nq > 0 ? Nq : 1);
+            int i = (int)(r % (Nq > 0 ? Nq : 1));
+            if (!buf)
+                continue;
+            row_three_pass(q + r * d, k + bh * Nk * (long)d, d,
+                           v + bh * Nk * (long)d, d,
+                           visible_keys_decode(i, Nq, Nk, causal), d, scale,
+                           buf, o + r * d, lse + r);
         }
         free(buf);
     }

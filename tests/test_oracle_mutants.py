@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_decode as dpins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_ref.c")
 
@@ -29,6 +30,11 @@ MUTANTS = {
     "causal_ignored": ("    if (!causal)\n        return n;", "    if (1)\n        return n;"),
     "online_rescale_dropped": ("acc[c] *= alpha;", "acc[c] *= 1.0;"),
     "online_sum_not_rescaled": ("l = l * alpha + psum;", "l = l + psum;"),
+    "decode_mask_from_the_first_key": ("last = (long)nk - nq + i;", "last = i;"),
+    "decode_mask_off_by_one": ("last = (long)nk - nq + i;", "last = (long)nk - nq + i - 1;"),
+    "decode_causal_ignored": ("    if (!causal)\n        return nk;", "    if (1)\n        return nk;"),
+    "decode_key_stride_of_queries": ("row_three_pass(q + r * d, k + bh * Nk * (long)d, d,",
+                                     "row_three_pass(q + r * d, k + bh * Nq * (long)d, d,"),
 }
 
 PINS = [
@@ -42,6 +48,11 @@ PINS = [
     lambda: pins.test_large_margin_rows_pick_the_argmax_value(),
     lambda: pins.test_online_recurrence_equals_three_pass(True, 37, 8, 11),
     lambda: pins.test_online_recurrence_equals_three_pass(False, 37, 8, 11),
+    lambda: dpins.test_decode_square_equals_fwd(True),
+    lambda: dpins.test_decode_batch_is_independent_heads(True),
+    lambda: dpins.test_decode_is_the_last_rows_of_the_square_problem(3),
+    lambda: dpins.test_decode_zero_queries_give_visible_means(True, 4, 9),
+    lambda: dpins.test_decode_zero_queries_give_visible_means(True, 12, 9),
 ]
 
 
