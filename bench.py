@@ -139,6 +139,113 @@ def cpu_baseline(w, inp, budget_s):
             "sample": f"{sample}; {flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
 
 
+def decode_flops(w):
+    """4 d flops per visible (query, key) pair."""
+    if w.causal:
+        vis = sum(min(w.Nk, max(0, w.Nk - w.Nq + i + 1)) for i in range(w.Nq))
+    else:
+        vis = w.Nq * w.Nk
+    return 4.0 * w.B * w.H * vis * w.d
+
+
+def decode_bytes(w, elem):
+    """Compulsory HBM bytes of a decode step: K and V read once, Q read, O
+    and lse written."""
+    return w.B * w.H * (2 * w.Nk * w.d * elem + w.Nq * (2 * w.d * elem + 4))
+
+
+def bench_decode(args, torch, fa):
+    """One step = one fa_decode_fwd call (split kernel + merge kernel) over a
+    decode workload resident in HBM; reported in GB/s of compulsory bytes."""
+    w = fa_inputs.decode_by_name(args.workload)
+    log(f"[bench] decode workload {w.name}: generating seeded inputs")
+    inp = fa_inputs.make_decode_workload(w)
+    elem = 2 if w.dtype == "bf16" else 4
+    code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+
+    def dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(x).to("cuda")
+
+    q, k, v = (dev(x) for x in inp.device_arrays())
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    splits = fa.fa_decode_num_splits(w.B, w.H, w.Nq, w.Nk, 0)
+    wsb = fa.fa_decode_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    log(f"[bench] {splits} key ranges per (b, h), workspace {wsb / 2**20:.2f} MiB")
+
+    def step():
+        fa.fa_decode_fwd(q, k, v, o, lse, ws, wsb, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, w.causal,
+                         code, 0)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)]
+    kern_ms = float(np.mean(per))
+    ms_per_step = wall * 1e3 / args.steps
+    nbytes = decode_bytes(w, elem)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    log(f"[bench] step mean {kern_ms:.4f} ms (median {np.median(per):.4f}, min {np.min(per):.4f}); "
+        f"wall {ms_per_step:.4f} ms/step; {achieved:.0f} GB/s = "
+        f"{100 * achieved / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f}")
+    result = {
+        "metric": f"attention decode GB/s (compulsory bytes), {w.name}",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "method": "split-kv decode", "via": "fa_decode_fwd",
+                   "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                   "splits": splits, "bytes_per_step": nbytes,
+                   "flops_per_step": decode_flops(w)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        t0 = time.perf_counter()
+        n = 0
+        while True:  # whole batches of heads until the budget is spent
+            b = n % w.B
+            oracle.attention_decode(inp.q[b], inp.k[b], inp.v[b], w.scale, w.causal)
+            n += 1
+            if time.perf_counter() - t0 > args.cpu_budget:
+                break
+        dt = time.perf_counter() - t0
+        cb = n * nbytes / w.B
+        result["cpu_baseline"] = {"value": round(cb / dt / 1e9, 3), "unit": "GB/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"{n} of {w.B} batch entries (all {w.H} heads each) "
+                                            f"in {dt:.1f} s, fp64"}
+        log(f"[bench] cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
 def compare_naive(torch, fa, reps=20, warmup=5):
     """Fused kernel against the unfused three-step method on the same inputs:
     one head of d=64 (the single-head shape of the pages' naive-versus-tiled
@@ -195,7 +302,10 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=fa_inputs.HEADLINE.name,
-                    choices=[w.name for w in fa_inputs.WORKLOADS])
+                    choices=[w.name for w in fa_inputs.WORKLOADS] +
+                    [w.name for w in fa_inputs.DECODE_WORKLOADS],
+                    help="a prefill workload (fa_fwd), or a decode_* workload (fa_decode_fwd, "
+                         "split-KV, measured in GB/s against the HBM peak)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--method", choices=["fused", "naive"], default="fused",
@@ -225,6 +335,9 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     if args.compare_naive:
         compare_naive(torch, fa)
+        return
+    if args.workload.startswith("decode_"):
+        bench_decode(args, torch, fa)
         return
 
     w = fa_inputs.by_name(args.workload)

@@ -11,8 +11,9 @@ here): numpy ``default_rng(seed)`` (PCG64), ``standard_normal`` drawn as
 float32 in the order Q, K, V.  The packed variable-length workload first
 draws its sequence lengths with ``integers(1, max_len, endpoint=True)``,
 then Q, K, V, and multiplies Q and K by 8 (exact in fp32 and in bf16, so it
-commutes with rounding).  bf16 tensors are the round-to-nearest-even
-rounding of the float32 draws.
+commutes with rounding).  Decode-shaped inputs draw Q [B, H, Nq, d], then
+K and V [B, H, Nk, d], the same way.  bf16 tensors are the
+round-to-nearest-even rounding of the float32 draws.
 """
 from __future__ import annotations
 
@@ -177,3 +178,51 @@ def workload_lengths(w: Workload) -> np.ndarray:
         return draw_lengths(np.random.default_rng(w.seed), w.nseq, w.max_len)
     return np.full(w.B, w.N, dtype=np.int64)
 
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """A decode step: Nq new queries per (batch, head) against Nk cached keys."""
+    name: str
+    dtype: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# Decode shapes: one new token for a batch of 16 sequences of 8K context;
+# one sequence of 128K context (32 heads only, so the key range must be
+# split to fill the GPU); 4 new tokens (a short causal block, as in
+# speculative decoding) for 8 sequences of 16K context.
+DECODE_WORKLOADS = [
+    DecodeWorkload("decode_b16h32q1k8192d128", "bf16", 16, 32, 1, 8192, 128, False, 7101),
+    DecodeWorkload("decode_b1h32q1k131072d128", "bf16", 1, 32, 1, 131072, 128, False, 7102),
+    DecodeWorkload("decode_b8h32q4k16384d128_causal", "bf16", 8, 32, 4, 16384, 128, True, 7103),
+]
+
+
+def decode_by_name(name: str) -> DecodeWorkload:
+    for w in DECODE_WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def make_decode(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int) -> Inputs:
+    """i.i.d. N(0, 1) Q [B, H, Nq, d], then K, V [B, H, Nk, d]."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    return _finish(q, k, v, dtype)
+
+
+def make_decode_workload(w: DecodeWorkload) -> Inputs:
+    return make_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)

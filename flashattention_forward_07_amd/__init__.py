@@ -9,6 +9,7 @@ fallback: if ``libfa355.so`` has not been built, loading fails loudly.
     o, lse = attention(q, k, v, causal=True)             # [B, H, N, d]
     o, lse = attention_varlen(q, k, v, cu_seqlens, max_seqlen, causal=True)
     o, lse = naive_attention(q, k, v, causal=True)       # unfused baseline
+    o, lse = decode_attention(q, k_cache, v_cache)        # q [B, H, Nq, d], split-KV
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ __all__ = [
     "FA_DTYPE_F32", "FA_DTYPE_BF16", "FAError", "fa_fwd", "fa_fwd_varlen",
     "fa_status_string", "fa_last_hip_error", "fa_version", "attention",
     "attention_varlen", "library_path", "load", "fa_naive_fwd", "fa_naive_workspace_bytes",
-    "naive_attention",
+    "naive_attention", "fa_decode_fwd", "fa_decode_workspace_bytes", "fa_decode_num_splits",
+    "decode_attention",
 ]
 
 FA_DTYPE_F32 = 0
@@ -66,6 +68,13 @@ def load():
     lib.fa_naive_fwd.restype = i32
     lib.fa_naive_workspace_bytes.argtypes = [i32, i32, i32]
     lib.fa_naive_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_decode_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, i32, i32, i32, i32, i32,
+                                  f32, i32, i32, i32, P]
+    lib.fa_decode_fwd.restype = i32
+    lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa_decode_num_splits.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_hip_error.argtypes = []
@@ -128,6 +137,29 @@ def fa_naive_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
                              int(bool(causal)), int(dtype), _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_naive_fwd")
+
+
+def fa_decode_workspace_bytes(B, H, Nq, Nk, d, num_splits=0) -> int:
+    """Workspace bytes fa_decode_fwd needs (0 when the keys are not split or
+    the sizes are out of range)."""
+    return int(load().fa_decode_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d),
+                                                int(num_splits)))
+
+
+def fa_decode_num_splits(B, H, Nq, Nk, num_splits=0) -> int:
+    """Key ranges per (b, h) that fa_decode_fwd uses (0 for sizes out of range)."""
+    return int(load().fa_decode_num_splits(int(B), int(H), int(Nq), int(Nk), int(num_splits)))
+
+
+def fa_decode_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, scale, causal,
+                  dtype, num_splits=0, stream=None) -> None:
+    """Enqueue the split-KV decode forward (partials in the workspace)."""
+    st = load().fa_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                              int(workspace_bytes), int(B), int(H), int(Nq), int(Nk), int(d),
+                              float(scale), int(bool(causal)), int(dtype), int(num_splits),
+                              _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_fwd")
 
 
 def fa_status_string(status: int) -> str:
@@ -205,4 +237,30 @@ def naive_attention(q, k, v, causal=False, scale=None, with_lse=True, workspace=
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if with_lse else None
     fa_naive_fwd(q, k, v, o, lse, workspace, workspace.numel() * workspace.element_size(), B, H,
                  N, d, scale, causal, _dtype_code(q), stream)
+    return o, lse
+
+
+def decode_attention(q, k, v, causal=False, scale=None, with_lse=True, num_splits=0,
+                     workspace=None, stream=None):
+    """Decode-shaped attention: q [B, H, Nq, d] (the newest Nq positions)
+    against k, v [B, H, Nk, d].  Allocates the split workspace with torch
+    unless one (uint8, large enough) is given."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    need = fa_decode_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if with_lse else None
+    fa_decode_fwd(q, k, v, o, lse, workspace, wbytes, B, H, Nq, Nk, d, scale, causal,
+                  _dtype_code(q), num_splits, stream)
     return o, lse

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fa355.h"
+#include "fa_decode_launch.h"
 #include "fa_fwd_launch.h"
 #include "fa_naive_launch.h"
 
@@ -203,6 +204,122 @@ FA_API int fa_naive_fwd(const void *q, const void *k, const void *v, void *o, fl
   return FA_OK;
 }
 
+// Split plan of fa_decode_fwd: key ranges of `chunk` keys (a multiple of
+// 16), `splits` of them per (b, h), and `qchunks` groups of queries.  With
+// num_splits = 0 the ranges are sized so that the chip gets ~4096 waves
+// (16 per compute unit) but no range is shorter than 256 keys; a request is
+// capped at Nk, and rounding the range up to 16 keys can lower it further.
+namespace {
+constexpr int kDecodeMaxQ = 64;
+constexpr long long kDecodeTargetWaves = 4096;
+constexpr int kDecodeMinKeys = 256;
+
+struct DecodePlan {
+  bool ok;
+  int splits, chunk, qchunks;
+  long long tasks;
+  size_t ws_bytes;  // 0 when splits == 1
+};
+
+DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  DecodePlan p{};
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || Nq > kDecodeMaxQ || num_splits < 0) return p;
+  if (d != 64 && d != 128) return p;
+  const long long bh = (long long)B * H;
+  if (Nk > (1 << 30) || bh * (Nq > Nk ? Nq : Nk) > kMaxRows) return p;
+  if (bh * Nq * d / 256 > kMaxGrid) return p;  // merge grid
+  const int nqw = fa355::decode_queries_per_wave(Nq);
+  p.qchunks = (Nq + nqw - 1) / nqw;
+  const long long items = bh * p.qchunks;
+  long long req = num_splits;
+  if (req == 0) {
+    req = (kDecodeTargetWaves + items - 1) / items;
+    const long long cap = Nk / kDecodeMinKeys > 1 ? Nk / kDecodeMinKeys : 1;
+    if (req > cap) req = cap;
+  }
+  if (req > Nk) req = Nk;
+  long long chunk = (Nk + req - 1) / req;
+  chunk = (chunk + 15) & ~15ll;
+  p.chunk = static_cast<int>(chunk);
+  p.splits = static_cast<int>((Nk + chunk - 1) / chunk);
+  p.tasks = items * p.splits;
+  if (p.tasks > 4 * kMaxGrid) return p;
+  const unsigned long long rows = (unsigned long long)bh * Nq;
+  p.ws_bytes = p.splits > 1 ? (size_t)(p.splits * rows * (unsigned long long)(d + 1) * 4ull) : 0;
+  p.ok = true;
+  return p;
+}
+}  // namespace
+
+FA_API size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  const DecodePlan p = decode_plan(B, H, Nq, Nk, d, num_splits);
+  return p.ok ? p.ws_bytes : 0;
+}
+
+FA_API int fa_decode_num_splits(int B, int H, int Nq, int Nk, int num_splits) {
+  const DecodePlan p = decode_plan(B, H, Nq, Nk, 64, num_splits);
+  return p.ok ? p.splits : 0;
+}
+
+FA_API int fa_decode_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                         void *workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk,
+                         int d, float scale, int causal, int dtype, int num_splits, void *stream) {
+  int st = value_checks(d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || num_splits < 0) return FA_ERR_SHAPE;
+  if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+  const DecodePlan p = decode_plan(B, H, Nq, Nk, d, num_splits);
+  if (!p.ok) return FA_ERR_SHAPE;
+  st = pointer_checks(q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  if (p.ws_bytes > 0) {
+    if (!workspace) return FA_ERR_NULL;
+    if (misaligned(workspace, 16)) return FA_ERR_ALIGN;
+    if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+  }
+  const long long bh = (long long)B * H;
+  const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  const size_t qbytes = (size_t)(bh * Nq) * d * esz, kbytes = (size_t)(bh * Nk) * d * esz;
+  const size_t lbytes = (size_t)(bh * Nq) * sizeof(float);
+  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
+      overlap(o, qbytes, v, kbytes))
+    return FA_ERR_ALIAS;
+  if (lse && (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+              overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes)))
+    return FA_ERR_ALIAS;
+  if (p.ws_bytes > 0 &&
+      (overlap(workspace, p.ws_bytes, q, qbytes) || overlap(workspace, p.ws_bytes, k, kbytes) ||
+       overlap(workspace, p.ws_bytes, v, kbytes) || overlap(workspace, p.ws_bytes, o, qbytes) ||
+       (lse && overlap(workspace, p.ws_bytes, lse, lbytes))))
+    return FA_ERR_ALIAS;
+  fa355::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  if (p.ws_bytes > 0) {
+    a.part_o = static_cast<float *>(workspace);
+    a.part_lse = a.part_o + (size_t)p.splits * (size_t)(bh * Nq) * d;
+  }
+  a.bh = bh;
+  a.nq = Nq;
+  a.nk = Nk;
+  a.splits = p.splits;
+  a.chunk = p.chunk;
+  a.qchunks = p.qchunks;
+  a.tasks = p.tasks;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  const hipError_t e = fa355::launch_decode(a, dtype, d, causal != 0,
+                                            reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 FA_API const char *fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
@@ -214,7 +331,8 @@ FA_API const char *fa_status_string(int status) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors need 16-byte alignment, lse 4-byte";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed (see fa_last_hip_error)";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than fa_naive_workspace_bytes";
+    case FA_ERR_WORKSPACE:
+      return "FA_ERR_WORKSPACE: workspace smaller than the entry point's *_workspace_bytes()";
     default: return "unknown status";
   }
 }

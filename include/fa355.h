@@ -19,8 +19,9 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates nothing, frees nothing and never synchronises; only
- *     fa_naive_fwd uses a workspace, which the caller provides.
+ *     library allocates nothing, frees nothing and never synchronises;
+ *     fa_naive_fwd and fa_decode_fwd (when it splits the keys) use a
+ *     workspace, which the caller provides.
  *   - A call validates its arguments on the host; on any error it returns a
  *     nonzero FA_ERR_* code and enqueues nothing.  On success it enqueues
  *     its kernel(s) on `stream` (a hipStream_t passed as void*; NULL = the
@@ -62,7 +63,7 @@ extern "C" {
 #define FA_ERR_ALIGN 6    /* a tensor pointer is misaligned */
 #define FA_ERR_ALIAS 7    /* an output overlaps an input or the other output */
 #define FA_ERR_HIP 8      /* the HIP launch failed; see fa_last_hip_error() */
-#define FA_ERR_WORKSPACE 9 /* workspace smaller than fa_naive_workspace_bytes() */
+#define FA_ERR_WORKSPACE 9 /* workspace smaller than the *_workspace_bytes() size */
 
 /*
  * fa_fwd -- attention forward over a fixed-length batch.
@@ -138,6 +139,53 @@ FA_API int fa_naive_fwd(const void *q, const void *k, const void *v, void *o,
  * rounded up to a multiple of 4 floats; 0 if a size is <= 0 or out of the
  * range fa_naive_fwd accepts. */
 FA_API size_t fa_naive_workspace_bytes(int B, int H, int N);
+
+/*
+ * fa_decode_fwd -- attention for decode-shaped problems: per (b, h), a few
+ * queries against a long key/value cache.  "Mini FlashAttention", section 1
+ * ties the causal mask to autoregressive decoding; the queries are taken to
+ * be the newest Nq positions of the Nk-long sequence.  The key range of each
+ * (b, h) is split into pieces processed in parallel, and the pieces' results
+ * are merged exactly through their log-sum-exp: with lse_s and O_s the
+ * softmax results over disjoint key sets, lse = ln sum_s exp(lse_s) and
+ * O = sum_s exp(lse_s - lse) O_s.
+ *
+ *   q, o        [B, H, Nq, d] contiguous, dtype elements
+ *   k, v        [B, H, Nk, d] contiguous, dtype elements (read only)
+ *   lse         [B, H, Nq] fp32 (written), or NULL
+ *   causal      0: every query sees all Nk keys; nonzero: query i
+ *               (0-based among the Nq) sees keys 0 .. Nk - Nq + i.  A query
+ *               that sees no key (Nq > Nk) gets O = 0 and lse = -inf.
+ *   num_splits  0: the library's choice (enough waves to fill the GPU, key
+ *               ranges of at least 256 keys); n > 0: at most n ranges per
+ *               (b, h) (ranges are whole multiples of 16 keys, so fewer may
+ *               result).  fa_decode_num_splits() gives the count used.
+ *   workspace   DEVICE buffer, 16-byte aligned, of at least
+ *               fa_decode_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+ *               bytes, owned by the caller (its contents are overwritten;
+ *               it must not overlap any tensor argument).  When that size
+ *               is 0 (one range per (b, h)) the workspace may be NULL.
+ *   workspace_bytes  its size (FA_ERR_WORKSPACE when too small)
+ *
+ * 1 <= Nq <= 64 and 1 <= Nk <= 2^30 (FA_ERR_SHAPE otherwise); B, H or Nq
+ * equal to 0 is an empty problem (FA_OK, nothing enqueued).  The same
+ * validation order and dtype conventions as fa_fwd.  Enqueues one kernel, or
+ * two when the keys are split.
+ */
+FA_API int fa_decode_fwd(const void *q, const void *k, const void *v, void *o,
+                         float *lse, void *workspace, size_t workspace_bytes,
+                         int B, int H, int Nq, int Nk, int d, float scale,
+                         int causal, int dtype, int num_splits, void *stream);
+
+/* Workspace bytes fa_decode_fwd needs for these sizes: splits x B H Nq x
+ * (d + 1) floats when the keys are split, else 0; also 0 when the sizes are
+ * out of range. */
+FA_API size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d,
+                                        int num_splits);
+
+/* Number of key ranges per (b, h) fa_decode_fwd uses for these sizes and
+ * num_splits request (0 when the sizes are out of range). */
+FA_API int fa_decode_num_splits(int B, int H, int Nq, int Nk, int num_splits);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 FA_API const char *fa_status_string(int status);

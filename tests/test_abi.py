@@ -36,8 +36,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert set(_declared()) == {"fa_fwd", "fa_fwd_varlen", "fa_naive_fwd",
-                                "fa_naive_workspace_bytes", "fa_status_string",
-                                "fa_last_hip_error", "fa_version"}
+                                "fa_naive_workspace_bytes", "fa_decode_fwd",
+                                "fa_decode_workspace_bytes", "fa_decode_num_splits",
+                                "fa_status_string", "fa_last_hip_error", "fa_version"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -145,6 +146,62 @@ def test_naive_rejects_bad_arguments(lib):
     assert _naive(lib, o=A) == c["FA_ERR_ALIAS"]
     assert _naive(lib, ws=A + 0x2000) == c["FA_ERR_ALIAS"]  # workspace over v
     assert _naive(lib, N=0) == 0 and _naive(lib, B=0, ws=None) == 0
+
+
+S = 0x10000  # spacing of the fake decode tensors
+
+
+def _decode(lib, q=A, k=A + S, v=A + 2 * S, o=A + 3 * S, lse=None, ws=A + 4 * S, ws_bytes=None,
+            B=1, H=1, Nq=1, Nk=64, d=64, scale=0.125, causal=0, dtype=BF16, splits=2):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_workspace_bytes(B, H, Nq, Nk, d, splits)
+    return lib.fa_decode_fwd(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, d,
+                             ctypes.c_float(scale), causal, dtype, splits, None)
+
+
+def test_decode_split_plan(lib):
+    # the library's choice: ~4096 waves, key ranges of at least 256 keys
+    assert lib.fa_decode_num_splits(16, 32, 1, 8192, 0) == 8
+    assert lib.fa_decode_num_splits(1, 32, 1, 131072, 0) == 128
+    assert lib.fa_decode_num_splits(64, 64, 1, 8192, 0) == 1
+    assert lib.fa_decode_num_splits(1, 1, 1, 100, 0) == 1
+    # 4 queries per wave: 16 query groups
+    assert lib.fa_decode_num_splits(1, 8, 64, 65536, 0) == 32
+    # requests: ranges are whole multiples of 16 keys, at most Nk of them
+    assert lib.fa_decode_num_splits(1, 1, 1, 100, 3) == 3     # 48 + 48 + 4
+    assert lib.fa_decode_num_splits(1, 1, 1, 100, 5) == 4     # 32 x 3 + 4
+    assert lib.fa_decode_num_splits(1, 1, 1, 16, 7) == 1
+    assert lib.fa_decode_num_splits(1, 1, 1, 1000, 10**6) == 63
+    for bad in ((0, 1, 1, 8, 0), (1, 1, 0, 8, 0), (1, 1, 65, 80, 0), (1, 1, 1, 0, 0),
+                (1, 1, 1, 8, -1), (1, 1, 1, (1 << 30) + 1, 0)):
+        assert lib.fa_decode_num_splits(*bad) == 0
+
+
+def test_decode_workspace_size(lib):
+    assert lib.fa_decode_workspace_bytes(1, 1, 1, 100, 64, 0) == 0
+    assert lib.fa_decode_workspace_bytes(2, 3, 5, 100, 128, 3) == 3 * 2 * 3 * 5 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(16, 32, 1, 8192, 128, 0) == 8 * 512 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(1, 1, 1, 64, 96, 2) == 0  # bad d
+
+
+def test_decode_rejects_bad_arguments(lib):
+    c = _status_codes()
+    assert _decode(lib, ws=None) == c["FA_ERR_NULL"]
+    assert _decode(lib, v=None) == c["FA_ERR_NULL"]
+    assert _decode(lib, ws=A + 4 * S + 8) == c["FA_ERR_ALIGN"]
+    assert _decode(lib, ws_bytes=100) == c["FA_ERR_WORKSPACE"]
+    assert _decode(lib, d=32) == c["FA_ERR_HEAD_DIM"]
+    assert _decode(lib, dtype=3) == c["FA_ERR_DTYPE"]
+    assert _decode(lib, scale=float("nan")) == c["FA_ERR_SCALE"]
+    assert _decode(lib, Nq=65) == c["FA_ERR_SHAPE"]
+    assert _decode(lib, Nk=0) == c["FA_ERR_SHAPE"]
+    assert _decode(lib, splits=-1) == c["FA_ERR_SHAPE"]
+    assert _decode(lib, o=A) == c["FA_ERR_ALIAS"]
+    assert _decode(lib, lse=A + 3 * S + 64) == c["FA_ERR_ALIAS"]  # lse over o
+    assert _decode(lib, ws=A + 2 * S) == c["FA_ERR_ALIAS"]  # workspace over v
+    # empty problems are a no-op; one key range needs no workspace
+    assert _decode(lib, B=0, ws=None) == 0 and _decode(lib, Nq=0, ws=None) == 0
+    assert lib.fa_decode_workspace_bytes(1, 1, 1, 64, 64, 1) == 0
 
 
 def test_python_binding_raises_on_error(lib):

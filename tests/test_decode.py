@@ -1,0 +1,82 @@
+"""GPU parity of the split-KV decode path (fa_decode_fwd, through the C ABI)
+against the fp64 oracle's decode-shaped entry: small shapes in full over
+both dtypes, both head dimensions, with and without the causal mask and for
+several split counts (one key range, the library's choice, a forced count,
+as many ranges as the keys allow); then the decode workloads at full size,
+compared in full (the oracle handles a decode step of these sizes in
+seconds).  The workspace is filled with NaN bytes before every call, so a
+partial result the merge reads but no wave wrote would show.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import flashattention_forward_07_amd as fa  # noqa: E402
+from tests import gpu_util as gu  # noqa: E402
+
+
+def _run(inp, scale, causal, num_splits):
+    q, k, v = gu.upload(inp)
+    B, H, Nq, d = inp.q.shape
+    Nk = inp.k.shape[2]
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, Nq), float("nan"), dtype=torch.float32, device="cuda")
+    need = fa.fa_decode_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")
+    code = fa.FA_DTYPE_BF16 if inp.dtype == "bf16" else fa.FA_DTYPE_F32
+    fa.fa_decode_fwd(q, k, v, o, lse, ws, need, B, H, Nq, Nk, d, scale, causal, code, num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+SHAPES = [(1, 1, 1, 1), (1, 2, 1, 300), (2, 1, 3, 129), (1, 1, 4, 64), (1, 2, 7, 257),
+          (1, 1, 12, 9), (2, 2, 64, 1000), (1, 1, 5, 5), (1, 3, 2, 4100)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [0, 1, 3, 1 << 20])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b%dh%dq%dk%d" % s)
+def test_decode_small_full(dtype, d, causal, splits, shape):
+    B, H, Nq, Nk = shape
+    print(f"case decode dtype={dtype} d={d} causal={causal} splits={splits} "
+          f"B={B} H={H} Nq={Nq} Nk={Nk}", flush=True)
+    inp = fa_inputs.make_decode(B, H, Nq, Nk, d, dtype, seed=3000 + Nq + Nk + d)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = _run(inp, scale, causal, splits)
+    o_ref, lse_ref = oracle.attention_decode(inp.q, inp.k, inp.v, scale, causal)
+    gu.compare(o, o_ref, lse, lse_ref, dtype, what=f"decode {shape} splits={splits}")
+
+
+def test_decode_split_count_does_not_change_the_result_beyond_rounding():
+    """Every split count computes the same function: results agree with each
+    other to the oracle bound, and the one-range result with the oracle."""
+    inp = fa_inputs.make_decode(2, 4, 3, 5000, 128, "bf16", seed=3333)
+    scale = float(np.float32(1.0 / math.sqrt(128)))
+    o_ref, lse_ref = oracle.attention_decode(inp.q, inp.k, inp.v, scale, True)
+    for splits in (1, 2, 7, 40, 313):
+        print(f"decode splits={splits}", flush=True)
+        o, lse = _run(inp, scale, True, splits)
+        gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"splits={splits}")
+
+
+@pytest.mark.parametrize("w", fa_inputs.DECODE_WORKLOADS, ids=lambda w: w.name)
+def test_decode_workload(w):
+    print(f"decode workload {w.name}", flush=True)
+    inp = fa_inputs.make_decode_workload(w)
+    print(f"  splits used: {fa.fa_decode_num_splits(w.B, w.H, w.Nq, w.Nk, 0)}", flush=True)
+    o, lse = _run(inp, w.scale, w.causal, 0)
+    o_ref, lse_ref = oracle.attention_decode(inp.q, inp.k, inp.v, w.scale, w.causal)
+    stats = gu.compare(o, o_ref, lse, lse_ref, w.dtype, what=w.name)
+    print(f"  {stats}", flush=True)
