@@ -68,18 +68,23 @@ def naive_bytes(N, B, H, d, elem, causal):
     return B * H * (N * (4 * d * elem + 4) + scores * (4 + 4 + 2 * elem))
 
 
-def kernel_source_hash():
+DECODE_SOURCES = ["flashattention_forward_07_amd/csrc/fa_decode.hip",
+                  "flashattention_forward_07_amd/csrc/fa_decode_launch.h",
+                  "flashattention_forward_07_amd/csrc/fa355_api.hip"]
+
+
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload_name):
+def committed_traffic(workload_name, prefix="fa_fwd", sources=None):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload_name}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload_name}_traffic.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -87,7 +92,7 @@ def committed_traffic(workload_name):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_sha256") != kernel_source_hash():
+    if vals.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -221,7 +226,7 @@ def bench_decode(args, torch, fa):
                    "flops_per_step": decode_flops(w)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+                     "traffic": committed_traffic(w.name, "fa_decode", DECODE_SOURCES)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -232,7 +237,8 @@ def bench_decode(args, torch, fa):
         n = 0
         while True:  # whole batches of heads until the budget is spent
             b = n % w.B
-            oracle.attention_decode(inp.q[b], inp.k[b], inp.v[b], w.scale, w.causal)
+            oracle.attention_decode(inp.q[b:b + 1], inp.k[b:b + 1], inp.v[b:b + 1], w.scale,
+                                    w.causal)
             n += 1
             if time.perf_counter() - t0 > args.cpu_budget:
                 break

@@ -206,12 +206,13 @@ FA_API int fa_naive_fwd(const void *q, const void *k, const void *v, void *o, fl
 
 // Split plan of fa_decode_fwd: key ranges of `chunk` keys (a multiple of
 // 16), `splits` of them per (b, h), and `qchunks` groups of queries.  With
-// num_splits = 0 the ranges are sized so that the chip gets ~4096 waves
-// (16 per compute unit) but no range is shorter than 256 keys; a request is
-// capped at Nk, and rounding the range up to 16 keys can lower it further.
+// num_splits = 0 the ranges are sized for about one streaming wave per SIMD
+// (1024 waves), or two when a wave carries 4 queries and has more arithmetic
+// per byte to hide; fewer, longer streams measured faster than more, shorter
+// ones.  No range is shorter than 256 keys.  A request is capped at Nk, and
+// rounding the range up to 16 keys can lower it further.
 namespace {
 constexpr int kDecodeMaxQ = 64;
-constexpr long long kDecodeTargetWaves = 4096;
 constexpr int kDecodeMinKeys = 256;
 
 struct DecodePlan {
@@ -233,7 +234,8 @@ DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d, int num_splits) {
   const long long items = bh * p.qchunks;
   long long req = num_splits;
   if (req == 0) {
-    req = (kDecodeTargetWaves + items - 1) / items;
+    const long long target = nqw >= 4 ? 2048 : 1024;
+    req = (target + items - 1) / items;
     const long long cap = Nk / kDecodeMinKeys > 1 ? Nk / kDecodeMinKeys : 1;
     if (req > cap) req = cap;
   }

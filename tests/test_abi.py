@@ -160,13 +160,15 @@ def _decode(lib, q=A, k=A + S, v=A + 2 * S, o=A + 3 * S, lse=None, ws=A + 4 * S,
 
 
 def test_decode_split_plan(lib):
-    # the library's choice: ~4096 waves, key ranges of at least 256 keys
-    assert lib.fa_decode_num_splits(16, 32, 1, 8192, 0) == 8
-    assert lib.fa_decode_num_splits(1, 32, 1, 131072, 0) == 128
+    # the library's choice: ~1024 waves (2048 with 4 queries per wave), key
+    # ranges of at least 256 keys
+    assert lib.fa_decode_num_splits(16, 32, 1, 8192, 0) == 2
+    assert lib.fa_decode_num_splits(1, 32, 1, 131072, 0) == 32
     assert lib.fa_decode_num_splits(64, 64, 1, 8192, 0) == 1
     assert lib.fa_decode_num_splits(1, 1, 1, 100, 0) == 1
-    # 4 queries per wave: 16 query groups
-    assert lib.fa_decode_num_splits(1, 8, 64, 65536, 0) == 32
+    assert lib.fa_decode_num_splits(1, 1, 1, 1000, 0) == 3
+    # 4 queries per wave: 16 query groups of 4
+    assert lib.fa_decode_num_splits(1, 8, 64, 65536, 0) == 16
     # requests: ranges are whole multiples of 16 keys, at most Nk of them
     assert lib.fa_decode_num_splits(1, 1, 1, 100, 3) == 3     # 48 + 48 + 4
     assert lib.fa_decode_num_splits(1, 1, 1, 100, 5) == 4     # 32 x 3 + 4
@@ -180,7 +182,7 @@ def test_decode_split_plan(lib):
 def test_decode_workspace_size(lib):
     assert lib.fa_decode_workspace_bytes(1, 1, 1, 100, 64, 0) == 0
     assert lib.fa_decode_workspace_bytes(2, 3, 5, 100, 128, 3) == 3 * 2 * 3 * 5 * 129 * 4
-    assert lib.fa_decode_workspace_bytes(16, 32, 1, 8192, 128, 0) == 8 * 512 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(16, 32, 1, 8192, 128, 0) == 2 * 512 * 129 * 4
     assert lib.fa_decode_workspace_bytes(1, 1, 1, 64, 96, 2) == 0  # bad d
 
 
