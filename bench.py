@@ -252,6 +252,57 @@ def bench_decode(args, torch, fa):
     print(json.dumps(result), flush=True)
 
 
+def _timed(torch, fn, reps, warmup):
+    for _ in range(warmup):
+        fn()
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def compare_short(torch, fa, reps=50, warmup=10):
+    """Many short bf16 sequences (one head each, causal): the one-tile path
+    (fa_fwd, N <= 128) against the general streaming kernel on the same data
+    (fa_fwd_varlen with equal lengths: with one head the packed and the
+    fixed layouts coincide) and the naive method.  Median launch times."""
+    print("| d | sequences | N | one-tile us | general kernel us | naive us | "
+          "one-tile GB/s | general / one-tile |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    for d in (64, 128):
+        for B in (1, 1024, 8192):
+            for N in (16, 64, 128):
+                inp = fa_inputs.make_fixed(B, 1, N, d, "bf16", seed=9500 + N + d)
+                q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+                           for x in inp.device_arrays())
+                scale = float(np.float32(1.0 / math.sqrt(d)))
+                o1, o2, o3 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+                l1 = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
+                l2, l3 = torch.empty_like(l1), torch.empty_like(l1)
+                cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
+                wsb = fa.fa_naive_workspace_bytes(B, 1, N)
+                ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+                code = fa.FA_DTYPE_BF16
+                t1 = _timed(torch, lambda: fa.fa_fwd(q, k, v, o1, l1, B, 1, N, d, scale, True,
+                                                     code), reps, warmup)
+                t2 = _timed(torch, lambda: fa.fa_fwd_varlen(q, k, v, o2, l2, cu, B, N, 1, d, scale,
+                                                            True, code), reps, warmup)
+                t3 = _timed(torch, lambda: fa.fa_naive_fwd(q, k, v, o3, l3, ws, wsb, B, 1, N, d,
+                                                           scale, True, code), reps, warmup)
+                diff = (o1.float() - o2.float()).abs().max().item()
+                if diff > 2e-2:
+                    raise SystemExit(f"one-tile and general kernel disagree by {diff}")
+                gbs = algorithmic_bytes(B * N, 1, d, 2) / (t1 * 1e-3) / 1e9
+                print(f"| {d} | {B} | {N} | {t1 * 1e3:.1f} | {t2 * 1e3:.1f} | {t3 * 1e3:.1f} | "
+                      f"{gbs:.0f} | {t2 / t1:.2f} |", flush=True)
+
+
 def compare_naive(torch, fa, reps=20, warmup=5):
     """Fused kernel against the unfused three-step method on the same inputs:
     one head of d=64 (the single-head shape of the pages' naive-versus-tiled
@@ -324,6 +375,10 @@ def main():
                     help="instead of the bench line, time the fused kernel against the naive "
                          "three-step method over a range of N (one head and 32 heads, d=64, "
                          "non-causal) and print a markdown table")
+    ap.add_argument("--compare-short", action="store_true",
+                    help="instead of the bench line, time the one-tile path fa_fwd takes for "
+                         "bf16 N <= 128 against the general streaming kernel and the naive "
+                         "method on many short sequences, and print a markdown table")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 1 GiB device copy (for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -341,6 +396,9 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     if args.compare_naive:
         compare_naive(torch, fa)
+        return
+    if args.compare_short:
+        compare_short(torch, fa)
         return
     if args.workload.startswith("decode_"):
         bench_decode(args, torch, fa)

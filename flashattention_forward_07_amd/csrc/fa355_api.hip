@@ -11,6 +11,7 @@
 #include "fa_decode_launch.h"
 #include "fa_fwd_launch.h"
 #include "fa_naive_launch.h"
+#include "fa_small_launch.h"
 
 namespace {
 
@@ -103,6 +104,16 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *l
   a.max_len = N;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
+  if (dtype == FA_DTYPE_BF16 && N <= fa355::kSmallMaxN) {
+    // the whole sequence is one key tile: the one-tile kernel
+    const hipError_t e = fa355::launch_small_bf16(a, d, causal != 0,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      g_last_hip = static_cast<int>(e);
+      return FA_ERR_HIP;
+    }
+    return FA_OK;
+  }
   return launch(a, dtype, d, causal, false, stream);
 }
 

@@ -1,0 +1,221 @@
+// fa_small.hip -- one-tile attention forward for short sequences (N <= 128),
+// bf16, on gfx950.
+//
+// When a whole sequence fits in one key tile, the streaming loop of the
+// general kernel has nothing to stream: "Mini FlashAttention", section 3
+// ("Part A", one-shot fused attention) computes S, the softmax and P V for
+// the entire tile at once, with no running max to rescale.  This kernel does
+// that, sized for many short sequences: the general kernel gives every
+// (batch, head) a 256-row query tile and a software pipeline whose start-up
+// dominates at N <= 128, so with thousands of short heads it ran slower
+// than even the unfused method.
+//
+// Workgroup: 4 waves and G = 4 / ceil(N / 32) heads (4 heads of N <= 32,
+// 2 of N <= 64, one otherwise); wave i owns 32 queries of head i / (waves
+// per head).  The workgroup stages the K and V rows of its heads in LDS once
+// (16-byte coalesced loads, zero rows past N), synchronises once, and then
+// every wave works alone:
+//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (lane l holds query l % 32 and
+//       keys 8 (r / 4) + 4 (l / 32) + r % 4 of each 32-key block in register
+//       r), K rows read from LDS with ds_read_b128 (reading K straight
+//       from L2 instead, to halve the LDS and double the workgroups per CU
+//       at d = 128, measured slower);
+//   the row max and sum over at most 128 keys in the lane plus one exchange
+//   with lane l ^ 32 (the other half of the same query); keys >= N and,
+//   causal, keys after the query score -inf;
+//   O^T = V^T P^T with the unnormalised weights, rounded to bf16, taken
+//   straight from the score registers as the B operand; the A operand is
+//   read with ds_read_b64_tr_b16 from the V rows in the order the score
+//   registers hold their keys (rows 4 h + 0..3 and 8 + 4 h + 0..3 of each
+//   16-key step);
+//   O = O^T / l in bf16 (round to nearest even), lse = m + ln l.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_common.h"
+#include "fa_small_launch.h"
+
+namespace fa355 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxN = 128;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef short i16x4v_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 through its builtin, so the compiler schedules the
+// reads and their waits: within each 16-lane group, lane i receives column i
+// of the four rows the group's lanes address (lane j of the group reads row
+// j / 4, columns 4 (j % 4) .. + 3).
+__device__ __forceinline__ u32x2_t tr_read(const uint16_t *p) {
+  const i16x4v_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4v_t *)(p));
+  return __builtin_bit_cast(u32x2_t, x);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_wg, int nb) {
+  constexpr int RSK = D + 8;   // K row stride in LDS (elements): 16-byte pad, conflict-free b128 reads
+  constexpr int RSV = D + 16;  // V row stride: 32-byte pad, conflict-free transposing reads
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kMaxN * RSK];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kMaxN * RSV];
+
+  const int n = a.n;
+  const int n_heads = a.batch * a.H;
+  const int h0 = blockIdx.x * heads_per_wg;  // first (sequence, head) of this workgroup
+  const int rows = heads_per_wg * nb;        // staged rows (nb = N rounded up to 32)
+  const uint16_t *kg = static_cast<const uint16_t *>(a.k);
+  const uint16_t *vg = static_cast<const uint16_t *>(a.v);
+
+  // ---- stage K and V rows of the workgroup's heads (zeros past N) ----
+  for (int c = threadIdx.x; c < rows * (D / 8); c += kThreads) {
+    const int row = c / (D / 8), col = 8 * (c % (D / 8));
+    const int slot = row / nb, key = row - slot * nb;
+    const int bh = h0 + slot;
+    u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    if (key < n && bh < n_heads) {
+      const int s = bh / a.H, hd = bh - s * a.H;
+      const long long off = (long long)s * a.seq_stride + (long long)hd * a.head_stride +
+                            (long long)key * a.row_stride + col;
+      kx = *reinterpret_cast<const u32x4_t *>(kg + off);
+      vx = *reinterpret_cast<const u32x4_t *>(vg + off);
+    }
+    *reinterpret_cast<u32x4_t *>(ks + row * RSK + col) = kx;
+    *reinterpret_cast<u32x4_t *>(vs + row * RSV + col) = vx;
+  }
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int wph = nb / 32;  // waves per head
+  const int slot = wv / wph, qb = wv - slot * wph;
+  const int bh = h0 + slot;
+  const bool active = slot < heads_per_wg && bh < n_heads;  // wave-uniform
+  const int qi = 32 * qb + l32;                             // this lane's query
+  long long base = 0, lbase = 0;
+  bf16x8_t qr[D / 16];
+  if (active) {
+    const int s = bh / a.H, hd = bh - s * a.H;
+    base = (long long)s * a.seq_stride + (long long)hd * a.head_stride;
+    lbase = (long long)s * a.lse_seq_stride + (long long)hd * a.lse_head_stride;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (qi < n) x = *reinterpret_cast<const u32x4_t *>(qg + (long long)qi * a.row_stride + 16 * c + 8 * h);
+      qr[c] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+
+  // key blocks this wave needs: all of the head's, or (causal) up to its own
+  const int nkb = CAUSAL ? qb + 1 : wph;
+  const int krow0 = slot * nb;  // first LDS row of this head
+
+  // ---- S^T blocks, masked, in log2 units ----
+  f32x16_t sc[kMaxN / 32];
+  float m = neg_inf();
+#pragma unroll
+  for (int kb = 0; kb < kMaxN / 32; ++kb) {
+    if (kb >= nkb) break;  // wave-uniform
+    f32x16_t acc = {};
+    const uint16_t *krow = ks + (krow0 + 32 * kb + l32) * RSK + 8 * h;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(krow + 16 * c);  // ds_read_b128
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qr[c], acc,
+                                                    0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * kb + block_key(r, h);
+      const bool vis = key < n && (!CAUSAL || key <= qi);
+      acc[r] = vis ? acc[r] * a.scale_log2 : neg_inf();
+      m = fmaxf(m, acc[r]);
+    }
+    sc[kb] = acc;
+  }
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float mu = (m == neg_inf()) ? 0.f : m;  // a query with no visible key
+  float l = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < kMaxN / 32; ++kb) {
+    if (kb >= nkb) break;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[kb][r] = exp2_fast(sc[kb][r] - mu);
+      l += sc[kb][r];
+    }
+  }
+  l += __shfl_xor(l, 32);
+
+  // ---- O^T = V^T P^T ----
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
+  const int g = lane >> 4, j = lane & 15;
+  // first transposing read: rows 4 (g / 2) + j / 4 of the 16-key step,
+  // columns 16 (g % 2) + 4 (j % 4); the second read is 8 rows further
+  const uint16_t *va = vs + (krow0 + 4 * (g >> 1) + (j >> 2)) * RSV + 16 * (g & 1) + 4 * (j & 3);
+#pragma unroll
+  for (int kb = 0; kb < kMaxN / 32; ++kb) {
+    if (kb >= nkb) break;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {  // 16-key steps: score registers 8 st .. 8 st + 7
+      bf16x8_t pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kb][8 * st + e];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t *ad = va + (32 * kb + 16 * st) * RSV + 32 * db;
+        const u32x2_t lo = tr_read(ad), hi = tr_read(ad + 8 * RSV);
+        const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[db],
+                                                        0, 0, 0);
+      }
+    }
+  }
+
+  // ---- O = O^T / l, lse ----
+  if (qi >= n) return;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  uint16_t *orow = static_cast<uint16_t *>(a.o) + base + (long long)qi * a.row_stride;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const bf16x4_t x = {(__bf16)(o[db][4 * gq] * inv), (__bf16)(o[db][4 * gq + 1] * inv),
+                          (__bf16)(o[db][4 * gq + 2] * inv), (__bf16)(o[db][4 * gq + 3] * inv)};
+      *reinterpret_cast<bf16x4_t *>(orow + 32 * db + 8 * gq + 4 * h) = x;
+    }
+  if (h == 0 && a.lse != nullptr)
+    a.lse[lbase + (long long)qi * a.lse_row_stride] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : neg_inf();
+}
+
+template <int D>
+hipError_t run(const FwdArgs &a, bool causal, hipStream_t st) {
+  const int nb = (a.n + 31) & ~31;
+  const int heads_per_wg = 4 / (nb / 32);  // 4, 2, 1, 1
+  const long long n_heads = (long long)a.batch * a.H;
+  const long long grid = (n_heads + heads_per_wg - 1) / heads_per_wg;
+  if (grid <= 0 || grid > 0x7fffffffll) return hipErrorInvalidValue;
+  if (causal)
+    hipLaunchKernelGGL((small_bf16<D, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a,
+                       heads_per_wg, nb);
+  else
+    hipLaunchKernelGGL((small_bf16<D, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a,
+                       heads_per_wg, nb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, hipStream_t stream) {
+  if (a.n <= 0 || a.n > kSmallMaxN) return hipErrorInvalidValue;
+  if (d == 64) return run<64>(a, causal, stream);
+  if (d == 128) return run<128>(a, causal, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa355

@@ -1,0 +1,18 @@
+// fa_small_launch.h -- internal interface of the one-tile kernel for short
+// sequences (fa_small.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fa_fwd_launch.h"
+
+namespace fa355 {
+
+// Longest sequence the one-tile kernel takes: one key tile.
+constexpr int kSmallMaxN = 128;
+
+// Fixed-length bf16 batches with 1 <= a.n <= kSmallMaxN (a.batch, a.H, the
+// strides, scale and pointers as for launch_fwd).
+hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa355

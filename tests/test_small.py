@@ -1,0 +1,82 @@
+"""GPU parity of the one-tile path that fa_fwd takes for bf16 sequences of
+N <= 128 (a whole sequence in one key tile; 4 heads per workgroup when
+N <= 32, 2 when N <= 64): every length around the 32-key block edges, head
+counts that leave the last workgroup partly filled, both head dimensions,
+with and without the causal mask, compared in full with the fp64 oracle.
+The outputs start as NaN so a row the kernel misses shows.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import flashattention_forward_07_amd as fa  # noqa: E402
+from tests import gpu_util as gu  # noqa: E402
+
+LENGTHS = [1, 2, 7, 16, 31, 32, 33, 63, 64, 65, 96, 100, 127, 128]
+
+
+def _run(inp, scale, causal):
+    q, k, v = gu.upload(inp)
+    B, H, N, d = inp.q.shape
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, fa.FA_DTYPE_BF16)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", LENGTHS)
+def test_one_tile_lengths(d, causal, N):
+    B, H = 3, 3  # 9 heads: the last workgroup holds 1 of 4 (N <= 32) or 1 of 2 (N <= 64)
+    print(f"case one-tile d={d} causal={causal} B={B} H={H} N={N}", flush=True)
+    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=5000 + N + d)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = _run(inp, scale, causal)
+    o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, scale, causal)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"one-tile N={N}")
+
+
+@pytest.mark.parametrize("N", [16, 64, 128])
+def test_one_tile_many_heads(N):
+    """Many short sequences: 4099 heads (not a multiple of the heads per
+    workgroup), sampled heads compared in full."""
+    B, H, d = 4099, 1, 64
+    print(f"case one-tile many heads N={N}", flush=True)
+    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=5100 + N)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = _run(inp, scale, True)
+    pick = np.array([0, 1, 2, 3, 4, 5, 1024, 2047, 4096, 4097, 4098])
+    o_ref, lse_ref = oracle.attention(inp.q[pick], inp.k[pick], inp.v[pick], scale, True)
+    idx = torch.from_numpy(pick).cuda()
+    gu.compare(gu.host(o[idx]), o_ref, gu.host(lse[idx]), lse_ref, "bf16", what=f"heads N={N}")
+    assert torch.isfinite(o.float()).all().item() and torch.isfinite(lse).all().item()
+
+
+def test_one_tile_and_general_kernel_meet_at_128():
+    """N = 128 runs the one-tile kernel and N = 129 the general one; both
+    match the oracle on the same data (the first 128 keys' problem is a
+    prefix of the second under the causal mask)."""
+    d = 128
+    inp = fa_inputs.make_fixed(2, 2, 129, d, "bf16", seed=5200)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o129, l129 = _run(inp, scale, True)
+    sub = fa_inputs.Inputs(inp.q[:, :, :128].copy(), inp.k[:, :, :128].copy(),
+                           inp.v[:, :, :128].copy(), "bf16", None,
+                           inp.q_bits[:, :, :128].copy(), inp.k_bits[:, :, :128].copy(),
+                           inp.v_bits[:, :, :128].copy())
+    o128, l128 = _run(sub, scale, True)
+    o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, scale, True)
+    gu.compare(o129, o_ref, l129, lse_ref, "bf16", what="N=129")
+    gu.compare(o128, o_ref[:, :, :128], l128, lse_ref[:, :, :128], "bf16", what="N=128")
