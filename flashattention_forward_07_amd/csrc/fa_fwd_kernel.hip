@@ -48,7 +48,8 @@
 // Lazy rescaling: the exponent reference is a past row max, and a tile is
 // first weighted against it without computing its own row max.  The tile is
 // kept if no lane's weights sum above 2^8; only otherwise is the row max
-// taken and the reference raised to it (O and l scaled by exp2(old - new)).
+// taken and the reference raised to a fixed margin above it (O and l scaled
+// by exp2(old - new)).
 // The result is unchanged in exact arithmetic (any reference cancels in
 // O / l), the weights stay <= 256, far from fp32 overflow, and most tiles
 // skip both the row max and the rescale.
@@ -88,6 +89,14 @@ namespace {
 // M(t), tile t + 2; 1 = end of V(t), tile t + 3.
 #ifndef FA_LOAD_AT
 #define FA_LOAD_AT 0
+#endif
+// When the softmax rebases its exponent reference on a row max, the new
+// reference sits this many log2 units above the max, so rows whose scores keep
+// growing slowly (wide score ranges) stay on the fast path longer.  The
+// reference cancels in O / l and in lse; weights then start at 2^-16 and only
+// terms more than ~110 log2 units below the row max underflow to zero.
+#ifndef FA_REF_MARGIN
+#define FA_REF_MARGIN 16.f
 #endif
 
 
@@ -487,9 +496,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       mx = pair_max(mx);
       // rebase when the row grew past the reference, or on its first finite score
       const bool bump = (mbl == neg_inf()) ? (mx > neg_inf()) : (mx > 0.f);
-      const float delta = bump ? mx : 0.f;
+      const float delta = bump ? mx + FA_REF_MARGIN : 0.f;
       if (bump) {
-        const float mbl_new = g + mx;
+        const float mbl_new = g + mx + FA_REF_MARGIN;
         alpha = exp2_fast(mbl - mbl_new);  // 0 when there was no reference
         mbl = mbl_new;
       }
