@@ -31,11 +31,16 @@
 // 16c + 8(e/4) + 4(l/32) + e%4, which is what lane l holds.
 //
 // LDS: K and V tiles stay row-major ([key][d], as in memory) in a 4-stage
-// ring.  Each wave moves 1/8 of every tile: its matrix phase M(t) starts by
-// issuing the global loads of tile t + 2 into registers, and its softmax phase
-// V(t) writes them into LDS, so global latency is hidden behind a phase.
-// (Direct global->LDS loads were tried: on this part each one stalls the
-// issuing wave for about 100 cycles.)  K operands are read with one
+// ring.  Each wave moves 1/8 of every tile with direct global->LDS loads
+// (global_load_lds_dwordx4, 16 bytes per lane into consecutive LDS slots),
+// issued in its softmax phase V(t) for tile t + 2 and awaited (vmcnt) at the
+// end of its next matrix phase, before the barrier that precedes the first
+// read: no staging registers, no LDS write instructions, and the matrix
+// phase issues no memory traffic at all.  (An earlier probe measured ~100
+// stall cycles per such load; those came from a compiler-inserted vmcnt(0)
+// before every later LDS read the compiler could not prove disjoint.  Here
+// all operand reads are inline assembly, which that pass does not track,
+// and the only waits are the explicit ones.)  K operands are read with one
 // ds_read_b128 per lane (the LDS serves 16 lanes of a b128 read per cycle;
 // a pair of ds_read_b64 was measured to conflict two ways, because a b64
 // read is served 32 lanes at a time and lanes l and l + 16 then share
@@ -84,11 +89,6 @@ namespace {
 #endif
 #ifndef FA_LOOKAHEAD
 #define FA_LOOKAHEAD 4
-#endif
-// Where a wave issues the global loads of its staging slots: 0 = start of
-// M(t), tile t + 2; 1 = end of V(t), tile t + 3.
-#ifndef FA_LOAD_AT
-#define FA_LOAD_AT 0
 #endif
 // When the softmax rebases its exponent reference on a row max, the new
 // reference sits this many log2 units above the max, so rows whose scores keep
@@ -263,64 +263,47 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     }
   }
 
-  // ---- K/V tile staging: global -> registers -> LDS ---------------------
-  // A tile is 2 * TILE bytes of LDS in 16-byte slots.  Wave wv moves chunks
-  // p = (wv * DPW + i) * 64 + lane, i.e. row p / CPR, chunk p % CPR: the
-  // global loads read each row's chunks in order (consecutive lanes,
-  // consecutive addresses, which the address unit takes fastest) and the LDS
-  // writes put chunk j of row r at its swizzled slot.
+  // ---- K/V tile staging: global -> LDS directly -------------------------
+  // A tile is 2 * TILE bytes of LDS in 16-byte slots.  Load i of wave wv
+  // fills the 1 KB of slots p = (wv * DPW + i) * 64 + lane (row p / CPR,
+  // slot p % CPR) of the K tile and of the V tile, one slot per lane, so each
+  // lane fetches the logical chunk that the XOR swizzle places in its slot:
+  // chunk (p % CPR) ^ swz(row).  Every lane of a row still reads that row's
+  // 256 bytes (a permutation of its chunks).
   int d_row[C::DPW];
-  const uint16_t *d_pk[C::DPW], *d_pv[C::DPW];  // source of the chunk in tile 0
-  const uint16_t *d_ck[C::DPW], *d_cv[C::DPW];  // its column in row 0 (ragged path)
-  uint32_t d_lk[C::DPW], d_lv[C::DPW];          // its LDS offsets within a stage
+  const uint16_t *e_pk[C::DPW], *e_pv[C::DPW];  // source of the slot in tile 0
+  const uint16_t *e_ck[C::DPW], *e_cv[C::DPW];  // its column in row 0 (ragged path)
 #pragma unroll
   for (int i = 0; i < C::DPW; ++i) {
     const int p = (wv * C::DPW + i) * kWave + lane;
-    const int row = p / C::CPR, chunk = p % C::CPR;
+    const int row = p / C::CPR, slot = p % C::CPR;
     d_row[i] = row;
-    d_ck[i] = kb + 8 * chunk;
-    d_cv[i] = vb + 8 * chunk;
-    d_pk[i] = d_ck[i] + (long long)row * rs;
-    d_pv[i] = d_cv[i] + (long long)row * rs;
-    d_lk[i] = row * C::ROWB + 16 * (chunk ^ C::swz_k(row));
-    d_lv[i] = C::TILE + row * C::ROWB + 16 * (chunk ^ C::swz_v(row));
+    e_ck[i] = kb + 8 * (slot ^ C::swz_k(row));
+    e_cv[i] = vb + 8 * (slot ^ C::swz_v(row));
+    e_pk[i] = e_ck[i] + (long long)row * rs;
+    e_pv[i] = e_cv[i] + (long long)row * rs;
   }
-  constexpr int NLD = 2 * C::DPW;  // loads per wave per tile: K slots, then V slots
-  u32x4_t stg[NLD];                // this wave's slots of the tile in flight
-  const uint16_t *src[NLD];        // their sources in the tile being loaded
-  auto prep_tile = [&](int t_) {
+  auto dma_tile = [&](int t_) {
     const int t = __builtin_amdgcn_readfirstlane(t_);
     const int key0 = t * kBN;
-    if (key0 + kBN <= n) {  // whole tile in range: one 64-bit add per load
-      const long long off = (long long)key0 * rs;
-#pragma unroll
-      for (int i = 0; i < C::DPW; ++i) {
-        src[i] = d_pk[i] + off;
-        src[C::DPW + i] = d_pv[i] + off;
-      }
-    } else {  // ragged last tile: rows past the end read row n - 1 (masked later)
-#pragma unroll
-      for (int i = 0; i < C::DPW; ++i) {
-        int key = key0 + d_row[i];
-        key = key < n ? key : n - 1;
-        const long long ro = (long long)key * rs;
-        src[i] = d_ck[i] + ro;
-        src[C::DPW + i] = d_cv[i] + ro;
-      }
-    }
-  };
-  auto load_tile = [&](int t) {
-    prep_tile(t);
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) stg[j] = *reinterpret_cast<const u32x4_t *>(src[j]);
-  };
-  auto store_tile = [&](int t_) {
-    const int t = __builtin_amdgcn_readfirstlane(t_);
     char *st = smem + (t & (kStages - 1)) * C::STAGE;
+    const bool whole = key0 + kBN <= n;
 #pragma unroll
     for (int i = 0; i < C::DPW; ++i) {
-      *reinterpret_cast<u32x4_t *>(st + d_lk[i]) = stg[i];
-      *reinterpret_cast<u32x4_t *>(st + d_lv[i]) = stg[C::DPW + i];
+      const uint16_t *sk, *sv;
+      if (whole) {
+        sk = e_pk[i] + (long long)key0 * rs;
+        sv = e_pv[i] + (long long)key0 * rs;
+      } else {  // ragged last tile: rows past the end read row n - 1 (masked later)
+        int key = key0 + d_row[i];
+        key = key < n ? key : n - 1;
+        sk = e_ck[i] + (long long)key * rs;
+        sv = e_cv[i] + (long long)key * rs;
+      }
+      const int reg = (wv * C::DPW + i) * 1024;  // this load's 1 KB of slots
+      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)sk, (FA_LDS void *)(st + reg), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)sv, (FA_LDS void *)(st + C::TILE + reg),
+                                       16, 0, 0);
     }
   };
 
@@ -407,15 +390,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       }
     });
   };
-  // M(t) first issues the global loads of this wave's share of tile t + 2 (the
-  // staging registers are free: their last LDS write finished before the
-  // previous barrier).
   auto m_phase = [&](int t) {
     const bool do_s = t < Tw;
     const bool do_pv = t >= 1 && t <= Tw;
-#if FA_LOAD_AT == 0
-    if (t + 2 < T) load_tile(t + 2);
-#endif
     if (!do_s && !do_pv) return;
     const uint32_t kbase = lds_base + (t & (kStages - 1)) * C::STAGE;
     const uint32_t vbase = lds_base + ((t - 1) & (kStages - 1)) * C::STAGE;
@@ -430,8 +407,6 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   };
 
   // V(t): softmax update of S_t -> P_t (bf16), l, rescaled O.
-  // V(t) also writes this wave's share of tile t + 2 (loaded during M(t)) into
-  // its LDS stage, whose previous tile t - 2 was last read two phases earlier.
   //
   // The reference is kept in the exp2 domain (mbl = scale log2(e) times a
   // past row max).  Every tile is first tried against the current reference
@@ -508,47 +483,36 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     }
     l_run = l_run * alpha + ps;
   };
+  // V(t) also sends tile t + 2 into its LDS stage, whose previous tile t - 2
+  // was last read two phases earlier: before the softmax at d = 128, after
+  // it at d = 64 (whose matrix phase is half as long, so its softmax phase
+  // has no slack to spare at the start; measured either way).
   auto v_phase = [&](int t) {
-    if (t + 2 < T) store_tile(t + 2);
+    if constexpr (D >= 128)
+      if (t + 2 < T) dma_tile(t + 2);
     if (t < Tw) v_softmax(t);
-#if FA_LOAD_AT == 1
-    if (t + 3 < T) load_tile(t + 3);
-#endif
+    if constexpr (D < 128)
+      if (t + 2 < T) dma_tile(t + 2);
   };
 
   // ---- prologue: tiles 0 and 1 in LDS (both in flight at once) -------------
-  load_tile(0);
-  if (T > 1) {
-    u32x4_t stg0[NLD];
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) stg0[j] = stg[j];
-    load_tile(1);
-    u32x4_t stg1[NLD];
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      stg1[j] = stg[j];
-      stg[j] = stg0[j];
-    }
-    store_tile(0);
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) stg[j] = stg1[j];
-    store_tile(1);
-  } else {
-    store_tile(0);
-  }
-#if FA_LOAD_AT != 0
-  if (T > 2) load_tile(2);
-#endif
+  dma_tile(0);
+  if (T > 1) dma_tile(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: both tiles have landed
   wg_barrier();
 
   // ---- ping-pong loop: phase ph; group g runs step ph - g ------------------
   for (int ph = 0; ph <= 2 * T + 1; ++ph) {
     const int step = ph - grp;
     if (step >= 0) {
-      if (!(step & 1))
+      if (!(step & 1)) {
         m_phase(step >> 1);
-      else
+        // the tile this wave sent in V(t - 1) must be in LDS before this
+        // barrier: group 0 reads it in the phase after next
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0
+      } else {
         v_phase(step >> 1);
+      }
     }
     wg_barrier();
   }
