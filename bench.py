@@ -268,19 +268,22 @@ def _timed(torch, fn, reps, warmup):
 
 
 def compare_short(torch, fa, reps=50, warmup=10):
-    """Many short bf16 sequences (one head each, causal): the one-tile path
-    (fa_fwd, N <= 128) against the general streaming kernel on the same data
+    """Many short sequences (one head each, causal, bf16 and fp32): fa_fwd,
+    which takes the one-tile kernels for N <= 128 (fp32 only while
+    latency-bound), against the general streaming kernel on the same data
     (fa_fwd_varlen with equal lengths: with one head the packed and the
     fixed layouts coincide) and the naive method.  Median launch times."""
-    print("| d | sequences | N | one-tile us | general kernel us | naive us | "
-          "one-tile GB/s | general / one-tile |")
-    print("|---|---:|---:|---:|---:|---:|---:|---:|")
-    for d in (64, 128):
-        for B in (1, 1024, 8192):
-            for N in (16, 64, 128):
-                inp = fa_inputs.make_fixed(B, 1, N, d, "bf16", seed=9500 + N + d)
-                q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
-                           for x in inp.device_arrays())
+    print("| dtype | d | sequences | N | fa_fwd path | fa_fwd us | general kernel us | naive us | "
+          "fa_fwd GB/s | general / fa_fwd |")
+    print("|---|---|---:|---:|---|---:|---:|---:|---:|---:|")
+    for dtype, d, B, N in [(dt, d, B, N) for dt in ("bf16", "f32") for d in (64, 128)
+                           for B in (1, 1024, 8192) for N in (16, 64, 128)]:
+                inp = fa_inputs.make_fixed(B, 1, N, d, dtype, seed=9500 + N + d)
+                if dtype == "bf16":
+                    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+                               for x in inp.device_arrays())
+                else:
+                    q, k, v = (torch.from_numpy(x).to("cuda") for x in inp.device_arrays())
                 scale = float(np.float32(1.0 / math.sqrt(d)))
                 o1, o2, o3 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
                 l1 = torch.empty((B, 1, N), dtype=torch.float32, device="cuda")
@@ -288,7 +291,8 @@ def compare_short(torch, fa, reps=50, warmup=10):
                 cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
                 wsb = fa.fa_naive_workspace_bytes(B, 1, N)
                 ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-                code = fa.FA_DTYPE_BF16
+                code = fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F32
+                elem = 2 if dtype == "bf16" else 4
                 t1 = _timed(torch, lambda: fa.fa_fwd(q, k, v, o1, l1, B, 1, N, d, scale, True,
                                                      code), reps, warmup)
                 t2 = _timed(torch, lambda: fa.fa_fwd_varlen(q, k, v, o2, l2, cu, B, N, 1, d, scale,
@@ -296,11 +300,14 @@ def compare_short(torch, fa, reps=50, warmup=10):
                 t3 = _timed(torch, lambda: fa.fa_naive_fwd(q, k, v, o3, l3, ws, wsb, B, 1, N, d,
                                                            scale, True, code), reps, warmup)
                 diff = (o1.float() - o2.float()).abs().max().item()
-                if diff > 2e-2:
+                if diff > (2e-2 if dtype == "bf16" else 2e-5):
                     raise SystemExit(f"one-tile and general kernel disagree by {diff}")
-                gbs = algorithmic_bytes(B * N, 1, d, 2) / (t1 * 1e-3) / 1e9
-                print(f"| {d} | {B} | {N} | {t1 * 1e3:.1f} | {t2 * 1e3:.1f} | {t3 * 1e3:.1f} | "
-                      f"{gbs:.0f} | {t2 / t1:.2f} |", flush=True)
+                gbs = algorithmic_bytes(B * N, 1, d, elem) / (t1 * 1e-3) / 1e9
+                # the library's rule: bf16 always one-tile; fp32 while latency-bound
+                path = ("one-tile" if dtype == "bf16" or N <= 32 or 4.0 * B * N * N * d <= 2 ** 28
+                        else "general")
+                print(f"| {dtype} | {d} | {B} | {N} | {path} | {t1 * 1e3:.1f} | {t2 * 1e3:.1f} | "
+                      f"{t3 * 1e3:.1f} | {gbs:.0f} | {t2 / t1:.2f} |", flush=True)
 
 
 def compare_naive(torch, fa, reps=20, warmup=5):

@@ -104,10 +104,18 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *l
   a.max_len = N;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
-  if (dtype == FA_DTYPE_BF16 && N <= fa355::kSmallMaxN) {
-    // the whole sequence is one key tile: the one-tile kernel
-    const hipError_t e = fa355::launch_small_bf16(a, d, causal != 0,
-                                                  reinterpret_cast<hipStream_t>(stream));
+  // The whole sequence is one key tile: the one-tile kernels.  bf16 always
+  // (ahead of the streaming kernel at every measured size); fp32 only while
+  // the problem is latency-bound -- N <= 32, or at most 2^28 flops in all --
+  // since its vector-ALU arithmetic is ~3 x slower per flop than the fp32
+  // matrix-core streaming kernel once many heads fill the GPU.
+  const double flops = 4.0 * (double)bh * N * (double)N * d;
+  const bool one_tile = N <= fa355::kSmallMaxN &&
+                        (dtype == FA_DTYPE_BF16 || N <= 32 || flops <= 268435456.0);
+  if (one_tile) {
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == FA_DTYPE_BF16 ? fa355::launch_small_bf16(a, d, causal != 0, st)
+                                                : fa355::launch_small_f32(a, d, causal != 0, st);
     if (e != hipSuccess) {
       g_last_hip = static_cast<int>(e);
       return FA_ERR_HIP;

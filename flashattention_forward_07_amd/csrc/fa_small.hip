@@ -1,5 +1,5 @@
-// fa_small.hip -- one-tile attention forward for short sequences (N <= 128),
-// bf16, on gfx950.
+// fa_small.hip -- one-tile attention forward for short sequences (N <= 128)
+// on gfx950: bf16 on the matrix cores, fp32 on the vector ALU.
 //
 // When a whole sequence fits in one key tile, the streaming loop of the
 // general kernel has nothing to stream: "Mini FlashAttention", section 3
@@ -193,6 +193,134 @@ __global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_
     a.lse[lbase + (long long)qi * a.lse_row_stride] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : neg_inf();
 }
 
+// ---- fp32 ------------------------------------------------------------------
+// fp32 has no fast matrix path worth its set-up at this size (the fp32
+// matrix cores and the vector ALU have the same peak), so this variant
+// spends its effort on latency instead: a workgroup of 256 threads takes 16
+// queries of one head (a one-head N = 128 problem spreads over 8 CUs), and
+// all arithmetic is plain fp32 FMA, which keeps the fp32 result within 1e-5.
+//   1. K rows (N <= 128, rows padded by 4 floats so 16 lanes reading 16 rows
+//      with 16-byte reads hit distinct banks) go to LDS; thread t owns query
+//      t / 16 and keys t % 16 + 16 i, i < 8, and forms their scores from its
+//      query row (registers) and the K rows;
+//   2. the row max and sum over the 16 threads of a query (shuffles), the
+//      weights into LDS;
+//   3. V replaces K in LDS; thread t forms O[q][4 (t % 16) .. + 3] (d = 64)
+//      or two such groups (d = 128) as the weighted sum over the keys.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void small_f32(FwdArgs a, int qblocks) {
+  constexpr int QB = 16;       // queries per workgroup
+  constexpr int RS = D + 4;    // LDS row stride (floats)
+  constexpr int CPT = D / 64;  // 4-column groups per thread in step 3
+  __shared__ __attribute__((aligned(16))) float kv[kMaxN * RS];
+  __shared__ __attribute__((aligned(16))) float pw[QB * kMaxN];
+
+  const int n = a.n;
+  const int bh = blockIdx.x / qblocks, qb = blockIdx.x - bh * qblocks;
+  const int s = bh / a.H, hd = bh - s * a.H;
+  const long long base = (long long)s * a.seq_stride + (long long)hd * a.head_stride;
+  const long long lbase = (long long)s * a.lse_seq_stride + (long long)hd * a.lse_head_stride;
+  const float *qg = static_cast<const float *>(a.q) + base;
+  const float *kg = static_cast<const float *>(a.k) + base;
+  const float *vg = static_cast<const float *>(a.v) + base;
+  const int t = threadIdx.x, ql = t >> 4, jj = t & 15;
+  const int qi = qb * QB + ql;  // this thread's query
+
+  auto stage = [&](const float *src) {  // rows past n are zeros
+    for (int c = t; c < n * (D / 4); c += kThreads) {
+      const int row = c / (D / 4), col = 4 * (c % (D / 4));
+      *reinterpret_cast<f32x4_t *>(kv + row * RS + col) =
+          *reinterpret_cast<const f32x4_t *>(src + (long long)row * a.row_stride + col);
+    }
+  };
+  stage(kg);
+  f32x4_t qr[D / 4];
+#pragma unroll
+  for (int c = 0; c < D / 4; ++c) {
+    qr[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (qi < n) qr[c] = *reinterpret_cast<const f32x4_t *>(qg + (long long)qi * a.row_stride + 4 * c);
+  }
+  __syncthreads();
+
+  // 1. scores of keys jj + 16 i
+  float sc[8];
+  float m = neg_inf();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = jj + 16 * i;
+    float acc = 0.f;
+    if (j < n) {
+      const float *kr = kv + j * RS;
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c) {
+        const f32x4_t kx = *reinterpret_cast<const f32x4_t *>(kr + 4 * c);
+        acc = __builtin_fmaf(qr[c][0], kx[0], acc);
+        acc = __builtin_fmaf(qr[c][1], kx[1], acc);
+        acc = __builtin_fmaf(qr[c][2], kx[2], acc);
+        acc = __builtin_fmaf(qr[c][3], kx[3], acc);
+      }
+    }
+    const bool vis = j < n && (!CAUSAL || j <= qi);
+    sc[i] = vis ? acc * a.scale_log2 : neg_inf();
+    m = fmaxf(m, sc[i]);
+  }
+  // 2. max and sum over the query's 16 threads
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float mu = (m == neg_inf()) ? 0.f : m;
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = exp2_fast(sc[i] - mu);
+    l += p;
+    pw[ql * kMaxN + jj + 16 * i] = p;
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off);
+  __syncthreads();  // every thread is done with K
+  stage(vg);
+  __syncthreads();
+
+  // 3. O[q][cols] = sum_j p_j V[j][cols]
+  f32x4_t o[CPT];
+#pragma unroll
+  for (int g = 0; g < CPT; ++g) o[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nj = CAUSAL ? (qb * QB + QB < n ? qb * QB + QB : n) : n;  // keys any query here sees
+  const float *pr = pw + ql * kMaxN;
+  for (int j = 0; j < nj; ++j) {
+    const float p = pr[j];
+#pragma unroll
+    for (int g = 0; g < CPT; ++g) {
+      const f32x4_t vx = *reinterpret_cast<const f32x4_t *>(kv + j * RS + 64 * g + 4 * jj);
+      o[g][0] = __builtin_fmaf(p, vx[0], o[g][0]);
+      o[g][1] = __builtin_fmaf(p, vx[1], o[g][1]);
+      o[g][2] = __builtin_fmaf(p, vx[2], o[g][2]);
+      o[g][3] = __builtin_fmaf(p, vx[3], o[g][3]);
+    }
+  }
+  if (qi >= n) return;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  float *orow = static_cast<float *>(a.o) + base + (long long)qi * a.row_stride;
+#pragma unroll
+  for (int g = 0; g < CPT; ++g)
+    *reinterpret_cast<f32x4_t *>(orow + 64 * g + 4 * jj) =
+        f32x4_t{o[g][0] * inv, o[g][1] * inv, o[g][2] * inv, o[g][3] * inv};
+  if (jj == 0 && a.lse != nullptr)
+    a.lse[lbase + (long long)qi * a.lse_row_stride] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : neg_inf();
+}
+
+template <int D>
+hipError_t run_f32(const FwdArgs &a, bool causal, hipStream_t st) {
+  const int qblocks = (a.n + 15) / 16;
+  const long long grid = (long long)a.batch * a.H * qblocks;
+  if (grid <= 0 || grid > 0x7fffffffll) return hipErrorInvalidValue;
+  if (causal)
+    hipLaunchKernelGGL((small_f32<D, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a, qblocks);
+  else
+    hipLaunchKernelGGL((small_f32<D, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a, qblocks);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t run(const FwdArgs &a, bool causal, hipStream_t st) {
   const int nb = (a.n + 31) & ~31;
@@ -210,6 +338,13 @@ hipError_t run(const FwdArgs &a, bool causal, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_small_f32(const FwdArgs &a, int d, bool causal, hipStream_t stream) {
+  if (a.n <= 0 || a.n > kSmallMaxN) return hipErrorInvalidValue;
+  if (d == 64) return run_f32<64>(a, causal, stream);
+  if (d == 128) return run_f32<128>(a, causal, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, hipStream_t stream) {
   if (a.n <= 0 || a.n > kSmallMaxN) return hipErrorInvalidValue;

@@ -15,4 +15,8 @@ constexpr int kSmallMaxN = 128;
 // strides, scale and pointers as for launch_fwd).
 hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, hipStream_t stream);
 
+// The same for fp32 batches (plain fp32 arithmetic, 16 queries per
+// workgroup).
+hipError_t launch_small_f32(const FwdArgs &a, int d, bool causal, hipStream_t stream);
+
 }  // namespace fa355

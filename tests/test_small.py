@@ -1,8 +1,9 @@
-"""GPU parity of the one-tile path that fa_fwd takes for bf16 sequences of
-N <= 128 (a whole sequence in one key tile; 4 heads per workgroup when
-N <= 32, 2 when N <= 64): every length around the 32-key block edges, head
-counts that leave the last workgroup partly filled, both head dimensions,
-with and without the causal mask, compared in full with the fp64 oracle.
+"""GPU parity of the one-tile paths that fa_fwd takes for sequences of
+N <= 128 (a whole sequence in one key tile; bf16: 4 heads per workgroup when
+N <= 32, 2 when N <= 64; fp32: 16 queries per workgroup): every length
+around the block edges, head counts that leave the last workgroup partly
+filled, both dtypes and head dimensions, with and without the causal mask,
+compared in full with the fp64 oracle.
 The outputs start as NaN so a row the kernel misses shows.
 """
 import math
@@ -30,22 +31,24 @@ def _run(inp, scale, causal):
     B, H, N, d = inp.q.shape
     o = torch.full_like(q, float("nan"))
     lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
-    fa.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, fa.FA_DTYPE_BF16)
+    code = fa.FA_DTYPE_BF16 if inp.dtype == "bf16" else fa.FA_DTYPE_F32
+    fa.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, code)
     torch.cuda.synchronize()
     return o, lse
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", LENGTHS)
-def test_one_tile_lengths(d, causal, N):
-    B, H = 3, 3  # 9 heads: the last workgroup holds 1 of 4 (N <= 32) or 1 of 2 (N <= 64)
-    print(f"case one-tile d={d} causal={causal} B={B} H={H} N={N}", flush=True)
-    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=5000 + N + d)
+def test_one_tile_lengths(dtype, d, causal, N):
+    B, H = 3, 3  # 9 heads: the last bf16 workgroup holds 1 of 4 (N <= 32) or 1 of 2 (N <= 64)
+    print(f"case one-tile {dtype} d={d} causal={causal} B={B} H={H} N={N}", flush=True)
+    inp = fa_inputs.make_fixed(B, H, N, d, dtype, seed=5000 + N + d)
     scale = float(np.float32(1.0 / math.sqrt(d)))
     o, lse = _run(inp, scale, causal)
     o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, scale, causal)
-    gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"one-tile N={N}")
+    gu.compare(o, o_ref, lse, lse_ref, dtype, what=f"one-tile {dtype} N={N}")
 
 
 @pytest.mark.parametrize("N", [16, 64, 128])
