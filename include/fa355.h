@@ -78,6 +78,12 @@ extern "C" {
  * to 0 is an empty problem: FA_OK, nothing enqueued, pointers not examined
  * (they may be NULL).  Validation order: dtype, d, scale, sizes, then
  * pointers (NULL, alignment, overlap).
+ *
+ * Short sequences (N <= 128: the whole sequence is one key tile) run a
+ * one-tile kernel that computes S, the softmax and P V at once ("Mini
+ * FlashAttention", section 3, the one-shot kernel): always for bf16, and for
+ * fp32 while the problem is small (N <= 32, or 4 B H N^2 d <= 2^28 flops).
+ * Results meet the same bounds either way.
  */
 FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o,
                   float *lse, int B, int H, int N, int d, float scale,
