@@ -52,12 +52,12 @@
 //
 // Lazy rescaling: the exponent reference is a past row max, and a tile is
 // first weighted against it without computing its own row max.  The tile is
-// kept if no lane's weights sum above 2^8; only otherwise is the row max
+// kept if no lane's weights sum above 2^32; only otherwise is the row max
 // taken and the reference raised to a fixed margin above it (O and l scaled
 // by exp2(old - new)).
 // The result is unchanged in exact arithmetic (any reference cancels in
-// O / l), the weights stay <= 256, far from fp32 overflow, and most tiles
-// skip both the row max and the rescale.
+// O / l), the weights stay <= 2^32, far from fp32 overflow even summed over
+// millions of keys, and most tiles skip both the row max and the rescale.
 //
 // Masking: keys at or past the sequence end score -inf (the pages fill
 // padded key rows with zeros, which would give them score 0; the definition
@@ -91,12 +91,18 @@ namespace {
 #define FA_LOOKAHEAD 4
 #endif
 // When the softmax rebases its exponent reference on a row max, the new
-// reference sits this many log2 units above the max, so rows whose scores keep
-// growing slowly (wide score ranges) stay on the fast path longer.  The
-// reference cancels in O / l and in lse; weights then start at 2^-16 and only
-// terms more than ~110 log2 units below the row max underflow to zero.
+// reference sits FA_REF_MARGIN log2 units above the max, and a tile stays on
+// the fast path while every lane's weights sum to at most FA_FAST_BOUND, so
+// scores may grow ~80 log2 units past a rebased max before the next rebase:
+// rows whose scores keep creeping up (wide score ranges) rarely pay the
+// second pass.  The reference cancels in O / l and in lse; weights start at
+// 2^-48, so only terms more than ~78 log2 units below the row max (relative
+// weight < 2^-78) underflow, and no weight exceeds 2^32.
 #ifndef FA_REF_MARGIN
-#define FA_REF_MARGIN 16.f
+#define FA_REF_MARGIN 48.f
+#endif
+#ifndef FA_FAST_BOUND
+#define FA_FAST_BOUND 4294967296.f
 #endif
 
 
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   // The reference is kept in the exp2 domain (mbl = scale log2(e) times a
   // past row max).  Every tile is first tried against the current reference
   // (fast path: no row max at all); it is accepted when no lane's weights sum
-  // above 2^8, so every weight stays <= 2^8.  Otherwise (scores outgrew the
+  // above 2^32, so every weight stays <= 2^32.  Otherwise (scores outgrew the
   // reference, or no reference yet) the row max is taken and the reference
   // rebased on it, with O and l rescaled by exp2(old - new).
   auto weights = [&](float d) {  // P = exp2(x - d) into pb; returns this lane's sum
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     bool slow = __builtin_amdgcn_ballot_w64(mbl == neg_inf()) != 0;
     if (!slow) {
       ps = weights(0.f);
-      slow = __builtin_amdgcn_ballot_w64(!(ps <= 256.f)) != 0;  // NaN / inf fail too
+      slow = __builtin_amdgcn_ballot_w64(!(ps <= FA_FAST_BOUND)) != 0;  // NaN / inf fail too
     }
     if (slow) {
       // row max of x: four independent max3 chains over 8 values, then combined
