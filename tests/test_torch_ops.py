@@ -1,4 +1,4 @@
-"""The PyTorch operators torch.ops.fa355.fwd / fwd_varlen.
+"""The PyTorch operators torch.ops.fa355.fwd / fwd_varlen / decode.
 
 CPU: registration, the fake (meta) implementations' output shapes and
 dtypes, and argument validation.  GPU: the operators return exactly what
@@ -20,6 +20,16 @@ import flashattention_forward_07_amd.torch_ops  # noqa: E402,F401  (registers th
 def test_ops_are_registered():
     assert hasattr(torch.ops.fa355, "fwd")
     assert hasattr(torch.ops.fa355, "fwd_varlen")
+    assert hasattr(torch.ops.fa355, "decode")
+
+
+def test_fake_shapes_decode():
+    q = torch.empty(2, 3, 4, 128, dtype=torch.bfloat16, device="meta")
+    k = torch.empty(2, 3, 1000, 128, dtype=torch.bfloat16, device="meta")
+    o, lse = torch.ops.fa355.decode(q, k, k, True, None, 0)
+    assert o.shape == q.shape and lse.shape == (2, 3, 4) and lse.dtype == torch.float32
+    with pytest.raises(ValueError):  # d differs
+        torch.ops.fa355.decode(q, k[..., :64], k[..., :64], False, None, 0)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -120,3 +130,27 @@ def test_op_matches_oracle():
     scale = float(np.float32(1 / math.sqrt(64)))
     o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, scale, True)
     gu.compare(o, o_ref, lse, lse_ref, "bf16", what="op")
+
+
+@gpu
+def test_decode_op_equals_direct_call_and_oracle():
+    _need_gpu()
+    import fa_inputs
+    import oracle
+    from tests import gpu_util as gu
+    inp = fa_inputs.make_decode(2, 2, 3, 700, 128, "bf16", seed=4321)
+    q, k, v = gu.upload(inp)
+    o, lse = torch.ops.fa355.decode(q, k, v, True, None, 3)
+    o2 = torch.empty_like(q)
+    lse2 = torch.empty(2, 2, 3, dtype=torch.float32, device="cuda")
+    need = fa.fa_decode_workspace_bytes(2, 2, 3, 700, 128, 3)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    scale = float(np.float32(1 / math.sqrt(128)))
+    fa.fa_decode_fwd(q, k, v, o2, lse2, ws, need, 2, 2, 3, 700, 128, 1 / math.sqrt(128), True,
+                     fa.FA_DTYPE_BF16, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    o_ref, lse_ref = oracle.attention_decode(inp.q, inp.k, inp.v, scale, True)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what="decode op")
+    torch.library.opcheck(torch.ops.fa355.decode.default, (q, k, v, True, None, 0),
+                          test_utils=("test_schema", "test_faketensor"))
