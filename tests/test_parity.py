@@ -191,16 +191,20 @@ def test_single_token_gives_v(dtype):
             np.testing.assert_allclose(gu.host(o), inp.v, rtol=2.0 ** -21, atol=0)
 
 
-def test_lse_is_optional_and_output_unchanged():
-    inp = fa_inputs.make_fixed(1, 4, 257, 128, "bf16", seed=13)
+@pytest.mark.parametrize("dtype,N", [("bf16", 257), ("bf16", 100), ("f32", 100), ("f32", 300)])
+def test_lse_is_optional_and_output_unchanged(dtype, N):
+    """With and without lse, on the streaming kernels (N > 128) and on the
+    one-tile kernels (N <= 128)."""
+    inp = fa_inputs.make_fixed(1, 4, N, 128, dtype, seed=13)
     o1, _ = gu.run_fixed(inp, 0.09, True, with_lse=True)
     o2, lse2 = gu.run_fixed(inp, 0.09, True, with_lse=False)
     assert lse2 is None
     assert torch.equal(o1, o2)
 
 
-def test_run_to_run_bitwise_determinism():
-    inp = fa_inputs.make_fixed(2, 8, 1000, 128, "bf16", seed=14)
+@pytest.mark.parametrize("dtype,N", [("bf16", 1000), ("bf16", 64), ("f32", 100)])
+def test_run_to_run_bitwise_determinism(dtype, N):
+    inp = fa_inputs.make_fixed(2, 8, N, 128, dtype, seed=14)
     outs = [gu.run_fixed(inp, 0.088, True) for _ in range(3)]
     for o, lse in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
