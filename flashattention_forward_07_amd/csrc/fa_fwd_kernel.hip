@@ -4,7 +4,8 @@
 // section 4 (with the initialise / loop / finalise structure of the
 // grasp.study lesson "The Complete Kernel: Initialization, Loop, and
 // Finalization"): per query row a running max m, denominator l and fp32
-// output accumulator O; each K/V tile of 64 keys gives scores S, the state is
+// output accumulator O; each K/V tile (64 keys at d = 128, 128 at d = 64)
+// gives scores S, the state is
 // rescaled by exp(m_old - m_new), P = exp(S - m) is added into l and P.V into
 // O, and O / l is formed once at the end.  Scores and P never leave
 // registers.
@@ -109,13 +110,21 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;  // 512
 constexpr int kBlockM = 32 * kWaves;      // 256 query rows
-constexpr int kBN = 64;                   // keys per tile
 constexpr int kStages = 4;
+
+#ifndef FA_BN_D64
+#define FA_BN_D64 128
+#endif
 
 template <int D>
 struct Bf16Tile {
+  // keys per tile: 64 at d = 128; at d = 64 the registers allow 128, which
+  // gives the matrix phase 32 products as at d = 128 and halves the per-tile
+  // costs (barriers, staging issue, loop control) per key
+  static constexpr int BN = D == 128 ? 64 : FA_BN_D64;
+  static_assert(BN == 64 || BN == 128, "keys per tile");
   static constexpr int ROWB = D * 2;              // bytes per K/V row
-  static constexpr int TILE = kBN * ROWB;         // bytes per K (or V) tile
+  static constexpr int TILE = BN * ROWB;          // bytes per K (or V) tile
   static constexpr int STAGE = 2 * TILE;          // K tile then V tile
   static constexpr int LDS = kStages * STAGE;
   static constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
@@ -231,6 +240,8 @@ __device__ __forceinline__ float pair_sum(float x) {  // sum with lane ^ 32
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) {
   using C = Bf16Tile<D>;
+  constexpr int kBN = C::BN;    // keys per tile
+  constexpr int KB = kBN / 32;  // 32-key blocks per tile
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
   const int tid = threadIdx.x;
@@ -341,14 +352,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   f32x16_t o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-  f32x16_t sc[2];
+  f32x16_t sc[KB];
   bf16x8_t pb[kBN / 16];
   const float sl2 = a.scale_log2;
 
   // M(t): S_t = K_t Q^T and O^T += V_{t-1}^T P_{t-1}^T, interleaved.  Step i
   // does S product (kb = i % 2, c = i / 2) and P.V product (db = i / 4,
   // c = i % 4); operands are read kLook steps ahead into a ring of buffers.
-  constexpr int NSTEP = D / 8;
+  constexpr int NSTEP = KB * (D / 16);  // = (D / 32) (kBN / 16) P.V products
   constexpr int kLook = FA_LOOKAHEAD;
   constexpr int NB = kLook + 1;
   auto m_body = [&](auto do_s, auto do_pv, uint32_t kbase, uint32_t vbase) {
@@ -364,11 +375,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     auto issue = [&](auto I) {
       constexpr int i = decltype(I)::value, b = i % NB;
       if constexpr (S) {
-        constexpr int kbk = i & 1, c = i >> 1;
+        constexpr int kbk = i % KB, c = i / KB;
         kr[b] = lds_read_b128<kbk * 32 * C::ROWB>(ka[c]);
       }
       if constexpr (PV) {
-        constexpr int db = i >> 2, c = i & 3;
+        constexpr int db = i / (kBN / 16), c = i % (kBN / 16);
         vr[b][0] = lds_read_tr16<16 * c * C::ROWB>(va[db]);
         vr[b][1] = lds_read_tr16<(16 * c + 8) * C::ROWB>(va[db]);
       }
@@ -385,12 +396,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       else
         lgkm_wait<RPS * ahead>(vr[b][0], vr[b][1]);
       if constexpr (S) {
-        constexpr int kbk = i & 1, c = i >> 1;
+        constexpr int kbk = i % KB, c = i / KB;
         sc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[b]), q[c],
                                                           c == 0 ? f32x16_t{} : sc[kbk], 0, 0, 0);
       }
       if constexpr (PV) {
-        constexpr int db = i >> 2, c = i & 3;
+        constexpr int db = i / (kBN / 16), c = i % (kBN / 16);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_bf16(vr[b][0], vr[b][1]), pb[c], o[db],
                                                         0, 0, 0);
       }
@@ -444,12 +455,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     // x = S scale log2(e) - g; keys past the end and (causal) after the query
     // are -inf
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < KB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[b][r] = __builtin_fmaf(sc[b][r], sl2, -g);
     if ((key0 + kBN > n) || (CAUSAL && key0 + kBN - 1 > qw0)) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < KB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * b + block_key(r, h);
@@ -464,9 +475,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     }
     if (slow) {
       // row max of x: four independent max3 chains over 8 values, then combined
-      float mq[4];
+      float mq[2 * KB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2 * KB; ++j) {
         const int b = j >> 1, r0 = 8 * (j & 1);
         float m = max3f(sc[b][r0], sc[b][r0 + 1], sc[b][r0 + 2]);
         m = max3f(m, sc[b][r0 + 3], sc[b][r0 + 4]);
@@ -474,6 +485,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
         mq[j] = max2f(m, sc[b][r0 + 7]);
       }
       float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
+#pragma unroll
+      for (int j = 4; j < 2 * KB; j += 2) mx = max3f(mx, mq[j], mq[j + 1]);
       mx = pair_max(mx);
       // rebase when the row grew past the reference, or on its first finite score
       const bool bump = (mbl == neg_inf()) ? (mx > neg_inf()) : (mx > 0.f);
@@ -491,8 +504,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   };
   // V(t) also sends tile t + 2 into its LDS stage, whose previous tile t - 2
   // was last read two phases earlier: before the softmax at d = 128, after
-  // it at d = 64 (whose matrix phase is half as long, so its softmax phase
-  // has no slack to spare at the start; measured either way).
+  // it at d = 64 (where the softmax phase is the longer of the two; measured
+  // either way).
   auto v_phase = [&](int t) {
     if constexpr (D >= 128)
       if (t + 2 < T) dma_tile(t + 2);
