@@ -112,17 +112,18 @@ constexpr int kThreads = kWave * kWaves;  // 512
 constexpr int kBlockM = 32 * kWaves;      // 256 query rows
 constexpr int kStages = 4;
 
-#ifndef FA_BN_D64
-#define FA_BN_D64 128
-#endif
+// Keys per K/V tile: 64 at d = 128.  At d = 64 the registers also allow
+// 128, which gives the matrix phase 32 products as at d = 128 and halves the
+// per-key share of the per-tile costs (barriers, staging issue, loop
+// control); it is taken when the longest sequence has at least
+// kWideMinLen tokens, since shorter sequences would mostly compute masked
+// keys of a wide tile.
+constexpr int kWideMinLen = 256;
 
-template <int D>
+template <int D, int BN_>
 struct Bf16Tile {
-  // keys per tile: 64 at d = 128; at d = 64 the registers allow 128, which
-  // gives the matrix phase 32 products as at d = 128 and halves the per-tile
-  // costs (barriers, staging issue, loop control) per key
-  static constexpr int BN = D == 128 ? 64 : FA_BN_D64;
-  static_assert(BN == 64 || BN == 128, "keys per tile");
+  static constexpr int BN = BN_;
+  static_assert(BN == 64 || (BN == 128 && D == 64), "keys per tile");
   static constexpr int ROWB = D * 2;              // bytes per K/V row
   static constexpr int TILE = BN * ROWB;          // bytes per K (or V) tile
   static constexpr int STAGE = 2 * TILE;          // K tile then V tile
@@ -237,9 +238,9 @@ __device__ __forceinline__ float pair_sum(float x) {  // sum with lane ^ 32
   return a + b;
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int BN, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) {
-  using C = Bf16Tile<D>;
+  using C = Bf16Tile<D, BN>;
   constexpr int kBN = C::BN;    // keys per tile
   constexpr int KB = kBN / 32;  // 32-key blocks per tile
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -557,18 +558,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, int BN, bool CAUSAL, bool VARLEN>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3(a.grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, BN, CAUSAL, VARLEN>), dim3(a.grid), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int BN>
 hipError_t launch_d(const FwdArgs &a, bool causal, bool varlen, hipStream_t stream) {
   if (causal)
-    return varlen ? launch<D, true, true>(a, stream) : launch<D, true, false>(a, stream);
-  return varlen ? launch<D, false, true>(a, stream) : launch<D, false, false>(a, stream);
+    return varlen ? launch<D, BN, true, true>(a, stream) : launch<D, BN, true, false>(a, stream);
+  return varlen ? launch<D, BN, false, true>(a, stream) : launch<D, BN, false, false>(a, stream);
 }
 
 }  // namespace
@@ -581,8 +582,10 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   const long long grid = (long long)a.batch * a.H * a.n_qtiles;
   if (grid > 0x7fffffffll || grid <= 0) return hipErrorInvalidValue;
   a.grid = (int)grid;
-  if (d == 64) return launch_d<64>(a, causal, varlen, stream);
-  if (d == 128) return launch_d<128>(a, causal, varlen, stream);
+  if (d == 64)
+    return a.max_len >= kWideMinLen ? launch_d<64, 128>(a, causal, varlen, stream)
+                                    : launch_d<64, 64>(a, causal, varlen, stream);
+  if (d == 128) return launch_d<128, 64>(a, causal, varlen, stream);
   return hipErrorInvalidValue;
 }
 

@@ -31,8 +31,10 @@ def _scale(d):
 
 # --- small shapes, full comparison ------------------------------------------
 
+# (N = 255 and 256 sit on either side of the length from which d = 64 takes
+# 128-key tiles)
 SHAPES = [(2, 3, 300), (1, 2, 64), (1, 1, 1), (1, 1, 129), (1, 2, 127), (2, 1, 65),
-          (1, 1, 513)]
+          (1, 1, 513), (1, 2, 255), (1, 1, 256)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -131,9 +133,11 @@ def test_workload_varlen():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_small_full(dtype, d, causal):
-    lengths = [1, 0, 127, 128, 129, 300, 2, 64]  # includes an empty sequence
-    rng = np.random.default_rng(5 + d)
+@pytest.mark.parametrize("lengths", [[1, 0, 127, 128, 129, 300, 2, 64],  # an empty sequence
+                                     [200, 17, 0, 129, 65, 255]],  # longest below 256
+                         ids=["max300", "max255"])
+def test_varlen_small_full(dtype, d, causal, lengths):
+    rng = np.random.default_rng((5 if len(lengths) == 8 else 7) + d)
     inp = fa_inputs.make_varlen(lengths, 3, d, dtype, rng)
     o, lse = gu.run_varlen(inp, _scale(d), causal)
     o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(d),
