@@ -31,20 +31,25 @@ __device__ __forceinline__ int block_key(int r, int h) { return 8 * (r >> 2) + 4
 // (hardware id i runs on XCD i % 8, as its (i / 8)-th workgroup there).  When
 // the number of (sequence, head) pairs is a multiple of 8, head h is pinned
 // to XCD h % 8, so all query tiles of a head share that XCD's L2 and its
-// K/V stream, and each XCD issues its tiles level by level, heaviest
-// (highest query tile) first across its heads, which balances the causal
-// triangle.  Otherwise the order is heaviest-first over all heads.
+// K/V stream.  Each XCD takes its heads in groups of G (G divides its head
+// count; G <= 0 means all of them) and issues a group's tiles level by level,
+// heaviest (highest query tile) first across the group's heads, which
+// balances the causal triangle; a small group keeps several running
+// workgroups on each head's K/V stream at once.  Otherwise the order is
+// heaviest-first over all heads.
 struct TileOrder {
   int bh;  // (sequence, head) pair
   int qi;  // 0 = heaviest query tile
 };
-__device__ __forceinline__ TileOrder tile_order(int i, int n_heads) {
+__device__ __forceinline__ TileOrder tile_order(int i, int n_heads, int n_qtiles, int G) {
   TileOrder o;
   if (n_heads % kXcds == 0) {
     const int hx = n_heads / kXcds;  // heads per XCD
     const int x = i % kXcds, r = i / kXcds;
-    o.bh = x + kXcds * (r % hx);
-    o.qi = r / hx;
+    if (G <= 0 || hx % G != 0) G = hx;
+    const int grp = r / (G * n_qtiles), rr = r - grp * (G * n_qtiles);
+    o.bh = x + kXcds * (grp * G + rr % G);
+    o.qi = rr / G;
   } else {
     o.bh = i % n_heads;
     o.qi = i / n_heads;
@@ -69,7 +74,7 @@ struct TileCoords {
 // Workgroup -> (sequence, head, query tile) in the order of tile_order.
 template <bool VARLEN>
 __device__ __forceinline__ TileCoords tile_coords(const FwdArgs &a, int block_m) {
-  const TileOrder to = tile_order(blockIdx.x, a.batch * a.H);
+  const TileOrder to = tile_order(blockIdx.x, a.batch * a.H, a.n_qtiles, a.order_group);
   const int bh = to.bh;
   const int qt = a.n_qtiles - 1 - to.qi;
   const int s = bh / a.H;

@@ -572,6 +572,21 @@ hipError_t launch_d(const FwdArgs &a, bool causal, bool varlen, hipStream_t stre
   return varlen ? launch<D, BN, false, true>(a, stream) : launch<D, BN, false, false>(a, stream);
 }
 
+// Heads of one XCD scheduled together (tile_order): the largest divisor of
+// its head count up to kGroupHeads, so that the 32 CUs of an XCD run about
+// four workgroups on each head's K/V stream at once.  Measured on the packed
+// 16-sequence causal workload (64 heads per XCD): 729 TFLOP/s with all heads
+// in one group, 878 with groups of 8, 882 with 4, 818 with 1; fixed-length
+// workloads within +-1 % of one group.
+constexpr int kGroupHeads = 8;
+int head_group(int n_heads) {
+  if (n_heads % kXcds != 0) return 0;
+  const int hx = n_heads / kXcds;
+  int g = hx < kGroupHeads ? hx : kGroupHeads;
+  while (hx % g != 0) --g;
+  return g;
+}
+
 }  // namespace
 
 hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
@@ -579,6 +594,7 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   if (dtype == 0) return launch_fwd_f32(a, d, causal, varlen, stream);
   if (dtype != 1) return hipErrorInvalidValue;
   a.n_qtiles = (a.max_len + kBlockM - 1) / kBlockM;
+  a.order_group = head_group(a.batch * a.H);
   const long long grid = (long long)a.batch * a.H * a.n_qtiles;
   if (grid > 0x7fffffffll || grid <= 0) return hipErrorInvalidValue;
   a.grid = (int)grid;

@@ -32,6 +32,7 @@ struct FwdArgs {
   int max_len;   // longest sequence (sizes the grid)
   int n_qtiles;  // query tiles per (sequence, head)  -- set by the launcher
   int grid;      // workgroups launched                -- set by the launcher
+  int order_group;  // heads of one XCD scheduled as a group (0: all of them) -- set by the launcher
   float scale;       // softmax scale applied to q.k
   float scale_log2;  // scale * log2(e), for exp2
 };

@@ -230,3 +230,50 @@ def test_empty_problem_enqueues_nothing():
     q = torch.zeros((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
     o, lse = fa.attention(q, q, q)
     assert o.shape == q.shape and lse.shape == (0, 2, 16)
+
+
+# --- head grouping per XCD: every (head, query tile) computed exactly once ----
+
+def _run_nan_filled(inp, scale, causal, varlen):
+    """Launch with O and lse filled with NaN, so that a tile the schedule
+    skipped shows up as NaN rather than as stale memory."""
+    q, k, v = gu.upload(inp)
+    o = torch.full_like(q, float("nan"))
+    code = fa.FA_DTYPE_BF16 if inp.dtype == "bf16" else fa.FA_DTYPE_F32
+    if varlen:
+        T, H, d = inp.q.shape
+        lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        cu = torch.from_numpy(inp.cu_seqlens).to("cuda")
+        max_len = int(np.max(np.diff(inp.cu_seqlens)))
+        fa.fa_fwd_varlen(q, k, v, o, lse, cu, inp.cu_seqlens.size - 1, max_len, H, d, scale,
+                         causal, code)
+    else:
+        B, H, N, d = inp.q.shape
+        lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+        fa.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, code)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("B,H,N", [(2, 64, 300), (1, 88, 260)],
+                         ids=["16_heads_per_xcd", "11_heads_per_xcd"])
+def test_many_heads_full(B, H, N):
+    """128 (sequence, head) pairs give each XCD 16 heads, scheduled in groups
+    of 8; 88 give it 11, which has no divisor up to 8 but 1.  Compared in
+    full against the oracle."""
+    d = 128
+    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=7100 + H)
+    o, lse = _run_nan_filled(inp, _scale(d), True, False)
+    o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, _scale(d), True)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"B{B} H{H} N{N}")
+
+
+def test_many_heads_varlen_full():
+    """8 packed sequences x 24 heads: 24 (sequence, head) pairs per XCD in
+    groups of 8, ragged lengths, compared in full."""
+    rng = np.random.default_rng(7200)
+    lengths = [300, 1, 257, 64, 511, 129, 0, 200]
+    inp = fa_inputs.make_varlen(lengths, 24, 64, "bf16", rng)
+    o, lse = _run_nan_filled(inp, _scale(64), True, True)
+    o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(64), True)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what="varlen 8 x 24 heads")
