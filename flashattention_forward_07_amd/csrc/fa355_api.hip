@@ -19,6 +19,7 @@ thread_local int g_last_hip = 0;
 
 constexpr long long kMaxRows = 1ll << 40;  // B*H*N bound keeps every offset in int64
 constexpr long long kMaxGrid = 0x7fffffffll;
+constexpr long long kMaxTokenElems = 1ll << 23;  // H * d of a packed token
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
@@ -132,6 +133,9 @@ FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, f
   if (st != FA_OK) return st;
   if (nseq < 0 || H < 0 || max_seqlen < 0) return FA_ERR_SHAPE;
   if (nseq == 0 || H == 0 || max_seqlen == 0) return FA_OK;
+  // a K/V tile's rows (up to 128 tokens of H * d elements) are addressed with
+  // 32-bit byte offsets
+  if ((long long)H * d > kMaxTokenElems) return FA_ERR_SHAPE;
   st = pointer_checks(q, k, v, o, lse);
   if (st != FA_OK) return st;
   if (!cu_seqlens) return FA_ERR_NULL;

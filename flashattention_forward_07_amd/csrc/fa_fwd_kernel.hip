@@ -288,40 +288,49 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   // lane fetches the logical chunk that the XOR swizzle places in its slot:
   // chunk (p % CPR) ^ swz(row).  Every lane of a row still reads that row's
   // 256 bytes (a permutation of its chunks).
+  // Source addresses: a wave-uniform tile base (key0 rows down, in scalar
+  // registers) plus a fixed 32-bit byte offset per lane; the host bounds the
+  // row stride so that 64 or 128 rows stay below 2^31 bytes.
   int d_row[C::DPW];
-  const uint16_t *e_pk[C::DPW], *e_pv[C::DPW];  // source of the slot in tile 0
-  const uint16_t *e_ck[C::DPW], *e_cv[C::DPW];  // its column in row 0 (ragged path)
+  uint32_t o_k[C::DPW], o_v[C::DPW];  // byte offset of the slot's source in a whole tile
+  uint32_t c_k[C::DPW], c_v[C::DPW];  // byte offset of its column within a row (ragged path)
+  const uint32_t rsb = static_cast<uint32_t>(a.row_stride) * 2u;  // bytes per key row
 #pragma unroll
   for (int i = 0; i < C::DPW; ++i) {
     const int p = (wv * C::DPW + i) * kWave + lane;
     const int row = p / C::CPR, slot = p % C::CPR;
     d_row[i] = row;
-    e_ck[i] = kb + 8 * (slot ^ C::swz_k(row));
-    e_cv[i] = vb + 8 * (slot ^ C::swz_v(row));
-    e_pk[i] = e_ck[i] + (long long)row * rs;
-    e_pv[i] = e_cv[i] + (long long)row * rs;
+    c_k[i] = 16u * (slot ^ C::swz_k(row));
+    c_v[i] = 16u * (slot ^ C::swz_v(row));
+    o_k[i] = c_k[i] + row * rsb;
+    o_v[i] = c_v[i] + row * rsb;
   }
   auto dma_tile = [&](int t_) {
     const int t = __builtin_amdgcn_readfirstlane(t_);
     const int key0 = t * kBN;
     char *st = smem + (t & (kStages - 1)) * C::STAGE;
-    const bool whole = key0 + kBN <= n;
+    const char *kt = reinterpret_cast<const char *>(kb + (long long)key0 * rs);
+    const char *vt = reinterpret_cast<const char *>(vb + (long long)key0 * rs);
+    if (key0 + kBN <= n) {
 #pragma unroll
-    for (int i = 0; i < C::DPW; ++i) {
-      const uint16_t *sk, *sv;
-      if (whole) {
-        sk = e_pk[i] + (long long)key0 * rs;
-        sv = e_pv[i] + (long long)key0 * rs;
-      } else {  // ragged last tile: rows past the end read row n - 1 (masked later)
-        int key = key0 + d_row[i];
-        key = key < n ? key : n - 1;
-        sk = e_ck[i] + (long long)key * rs;
-        sv = e_cv[i] + (long long)key * rs;
+      for (int i = 0; i < C::DPW; ++i) {
+        const int reg = (wv * C::DPW + i) * 1024;
+        __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(kt + o_k[i]),
+                                         (FA_LDS void *)(st + reg), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(vt + o_v[i]),
+                                         (FA_LDS void *)(st + C::TILE + reg), 16, 0, 0);
       }
-      const int reg = (wv * C::DPW + i) * 1024;  // this load's 1 KB of slots
-      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)sk, (FA_LDS void *)(st + reg), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)sv, (FA_LDS void *)(st + C::TILE + reg),
-                                       16, 0, 0);
+    } else {
+      const int last = n - 1 - key0;
+#pragma unroll
+      for (int i = 0; i < C::DPW; ++i) {
+        const uint32_t rb = static_cast<uint32_t>(d_row[i] < last ? d_row[i] : last) * rsb;
+        const int reg = (wv * C::DPW + i) * 1024;
+        __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(kt + (rb + c_k[i])),
+                                         (FA_LDS void *)(st + reg), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(vt + (rb + c_v[i])),
+                                         (FA_LDS void *)(st + C::TILE + reg), 16, 0, 0);
+      }
     }
   };
 

@@ -107,7 +107,9 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o,
  * length above max_seqlen (rows past max_seqlen would be left unwritten).
  * o must not overlap q, k, v or lse (only exact pointer equality is
  * detected here, since T is not known on the host).  nseq, H or max_seqlen
- * equal to 0 is an empty problem, as for fa_fwd.
+ * equal to 0 is an empty problem, as for fa_fwd.  H d above 2^23 elements
+ * per token is FA_ERR_SHAPE (key rows of a tile are addressed with 32-bit
+ * byte offsets).
  */
 FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o,
                          float *lse, const int *cu_seqlens, int nseq,

@@ -112,6 +112,9 @@ def test_varlen_rejects_bad_arguments(lib):
     assert _fwd_varlen(lib, dtype=7) == c["FA_ERR_DTYPE"]
     assert _fwd_varlen(lib, o=A) == c["FA_ERR_ALIAS"]
     assert _fwd_varlen(lib, nseq=1 << 20, max_seqlen=1 << 30, H=64) == c["FA_ERR_SHAPE"]
+    # a packed token of more than 2^23 elements (H d) is out of range
+    assert _fwd_varlen(lib, H=(1 << 23) // 128 + 1, d=128) == c["FA_ERR_SHAPE"]
+    assert _fwd_varlen(lib, H=(1 << 23) // 64 + 1, d=64) == c["FA_ERR_SHAPE"]
     assert _fwd_varlen(lib, nseq=0) == 0
     assert _fwd_varlen(lib, max_seqlen=0) == 0
 
