@@ -277,3 +277,15 @@ def test_many_heads_varlen_full():
     o, lse = _run_nan_filled(inp, _scale(64), True, True)
     o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(64), True)
     gu.compare(o, o_ref, lse, lse_ref, "bf16", what="varlen 8 x 24 heads")
+
+
+def test_varlen_wide_token_rows():
+    """512 heads of d = 128: a packed token row is 128 KB, so the staging
+    offsets of a K/V tile reach ~16 MB (they are 32-bit byte offsets from the
+    tile's base); 1024 (sequence, head) pairs put 128 on each XCD."""
+    rng = np.random.default_rng(7300)
+    lengths = [300, 70]
+    inp = fa_inputs.make_varlen(lengths, 512, 128, "bf16", rng)
+    o, lse = _run_nan_filled(inp, _scale(128), True, True)
+    o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(128), True)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what="varlen 2 x 512 heads")
