@@ -238,21 +238,34 @@ __device__ __forceinline__ float pair_sum(float x) {  // sum with lane ^ 32
   return a + b;
 }
 
-template <int D, int BN, bool CAUSAL, bool VARLEN>
+// SPLIT: the key range is split instead of the query rows.  The workgroup
+// owns 128 query rows; waves w and w + 4 hold the same 32 rows, group 0
+// streams the first half of the K/V tiles and group 1 the second half, each
+// through an LDS ring of its own, and at the end group 1 hands its O, l and
+// exponent reference to group 0 through LDS, which merges the two partial
+// results (each term weighted by 2^(its reference - the larger one)) before
+// the final O / l.  It halves the serial key loop of a workgroup, for
+// problems whose grid would leave most compute units idle.
+template <int D, int BN, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) {
   using C = Bf16Tile<D, BN>;
   constexpr int kBN = C::BN;    // keys per tile
   constexpr int KB = kBN / 32;  // 32-key blocks per tile
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  constexpr int kRows = SPLIT ? kBlockM / 2 : kBlockM;  // query rows of the workgroup
+  constexpr int kCopyWaves = SPLIT ? kWaves / 2 : kWaves;  // waves that stage one ring
+  constexpr int DPW = C::TILE / (1024 * kCopyWaves);  // staging loads per wave per tensor
+  static_assert(DPW >= 1 && C::TILE % (1024 * kCopyWaves) == 0, "tile / workgroup mismatch");
+  __shared__ __attribute__((aligned(1024))) char smem[SPLIT ? 2 * C::LDS : C::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const int grp = wv >> 2;  // ping-pong group
+  const int rw = SPLIT ? (wv & 3) : wv;  // row slot (and staging slot) of this wave
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const TileCoords tc = tile_coords<VARLEN>(a, kBlockM);
+  const TileCoords tc = tile_coords<VARLEN>(a, kRows);
   const int n = tc.n, m0 = tc.m0;
   if (m0 >= n) return;  // uniform over the workgroup, before any barrier
 
@@ -261,13 +274,25 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   const uint16_t *vb = reinterpret_cast<const uint16_t *>(a.v) + tc.base;
   const long long rs = a.row_stride;
 
-  const int n_kv = CAUSAL ? (n < m0 + kBlockM ? n : m0 + kBlockM) : n;
+  const int n_kv = CAUSAL ? (n < m0 + kRows ? n : m0 + kRows) : n;
   const int T = (n_kv + kBN - 1) / kBN;  // K/V tiles of the workgroup
-  const int qw0 = m0 + 32 * wv;          // first query row of this wave
+  // The loop counts steps: step t of a group is K/V tile lo + t.  Without
+  // the split both groups step through all T tiles.
+  const int T0 = SPLIT ? (T + 1) / 2 : T;  // steps of group 0 (the longer share)
+  const int lo = (SPLIT && grp) ? T0 : 0;
+  const int Tg = SPLIT ? (grp ? T - T0 : T0) : T;  // steps of this wave's group
+  const int qw0 = m0 + 32 * rw;          // first query row of this wave
   const int qrow = qw0 + l32;            // this lane's query row
-  // tiles this wave works on (causal: none entirely above its diagonal)
+  // steps this wave works on (causal: no tile entirely above its diagonal)
   int Tw = 0;
-  if (qw0 < n) Tw = CAUSAL ? ((qw0 + 31) / kBN + 1 < T ? (qw0 + 31) / kBN + 1 : T) : T;
+  if (qw0 < n) {
+    const int last = CAUSAL ? ((qw0 + 31) / kBN + 1 < T ? (qw0 + 31) / kBN + 1 : T) : T;
+    if constexpr (SPLIT)
+      Tw = last - lo < 0 ? 0 : (last - lo < Tg ? last - lo : Tg);
+    else
+      Tw = last;
+  }
+  const int ring = SPLIT ? grp * C::LDS : 0;  // this group's LDS ring
 
   // ---- resident Q^T (B operand): lane holds Q[qrow][16c + 8h .. +7] ---------
   bf16x8_t q[D / 16];
@@ -291,13 +316,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   // Source addresses: a wave-uniform tile base (key0 rows down, in scalar
   // registers) plus a fixed 32-bit byte offset per lane; the host bounds the
   // row stride so that 64 or 128 rows stay below 2^31 bytes.
-  int d_row[C::DPW];
-  uint32_t o_k[C::DPW], o_v[C::DPW];  // byte offset of the slot's source in a whole tile
-  uint32_t c_k[C::DPW], c_v[C::DPW];  // byte offset of its column within a row (ragged path)
+  int d_row[DPW];
+  uint32_t o_k[DPW], o_v[DPW];  // byte offset of the slot's source in a whole tile
+  uint32_t c_k[DPW], c_v[DPW];  // byte offset of its column within a row (ragged path)
   const uint32_t rsb = static_cast<uint32_t>(a.row_stride) * 2u;  // bytes per key row
 #pragma unroll
-  for (int i = 0; i < C::DPW; ++i) {
-    const int p = (wv * C::DPW + i) * kWave + lane;
+  for (int i = 0; i < DPW; ++i) {
+    const int p = (rw * DPW + i) * kWave + lane;
     const int row = p / C::CPR, slot = p % C::CPR;
     d_row[i] = row;
     c_k[i] = 16u * (slot ^ C::swz_k(row));
@@ -307,14 +332,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   }
   auto dma_tile = [&](int t_) {
     const int t = __builtin_amdgcn_readfirstlane(t_);
-    const int key0 = t * kBN;
-    char *st = smem + (t & (kStages - 1)) * C::STAGE;
+    const int key0 = (lo + t) * kBN;
+    char *st = smem + ring + (t & (kStages - 1)) * C::STAGE;
     const char *kt = reinterpret_cast<const char *>(kb + (long long)key0 * rs);
     const char *vt = reinterpret_cast<const char *>(vb + (long long)key0 * rs);
     if (key0 + kBN <= n) {
 #pragma unroll
-      for (int i = 0; i < C::DPW; ++i) {
-        const int reg = (wv * C::DPW + i) * 1024;
+      for (int i = 0; i < DPW; ++i) {
+        const int reg = (rw * DPW + i) * 1024;
         __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(kt + o_k[i]),
                                          (FA_LDS void *)(st + reg), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(vt + o_v[i]),
@@ -323,9 +348,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     } else {
       const int last = n - 1 - key0;
 #pragma unroll
-      for (int i = 0; i < C::DPW; ++i) {
+      for (int i = 0; i < DPW; ++i) {
         const uint32_t rb = static_cast<uint32_t>(d_row[i] < last ? d_row[i] : last) * rsb;
-        const int reg = (wv * C::DPW + i) * 1024;
+        const int reg = (rw * DPW + i) * 1024;
         __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(kt + (rb + c_k[i])),
                                          (FA_LDS void *)(st + reg), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const FA_GLOBAL void *)(vt + (rb + c_v[i])),
@@ -421,8 +446,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     const bool do_s = t < Tw;
     const bool do_pv = t >= 1 && t <= Tw;
     if (!do_s && !do_pv) return;
-    const uint32_t kbase = lds_base + (t & (kStages - 1)) * C::STAGE;
-    const uint32_t vbase = lds_base + ((t - 1) & (kStages - 1)) * C::STAGE;
+    const uint32_t kbase = lds_base + ring + (t & (kStages - 1)) * C::STAGE;
+    const uint32_t vbase = lds_base + ring + ((t - 1) & (kStages - 1)) * C::STAGE;
     __builtin_amdgcn_s_setprio(FA_PRIO_M);
     if (do_s && do_pv)
       m_body(std::true_type{}, std::true_type{}, kbase, vbase);
@@ -460,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
     return (pq[0] + pq[1]) + (pq[2] + pq[3]);
   };
   auto v_softmax = [&](int t) {
-    const int key0 = t * kBN;
+    const int key0 = (lo + t) * kBN;
     const float g = (mbl == neg_inf()) ? 0.f : mbl;  // ghost-row guard
     // x = S scale log2(e) - g; keys past the end and (causal) after the query
     // are -inf
@@ -518,20 +543,20 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   // either way).
   auto v_phase = [&](int t) {
     if constexpr (D >= 128)
-      if (t + 2 < T) dma_tile(t + 2);
+      if (t + 2 < Tg) dma_tile(t + 2);
     if (t < Tw) v_softmax(t);
     if constexpr (D < 128)
-      if (t + 2 < T) dma_tile(t + 2);
+      if (t + 2 < Tg) dma_tile(t + 2);
   };
 
   // ---- prologue: tiles 0 and 1 in LDS (both in flight at once) -------------
-  dma_tile(0);
-  if (T > 1) dma_tile(1);
+  if (!SPLIT || Tg > 0) dma_tile(0);
+  if (Tg > 1) dma_tile(1);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: both tiles have landed
   wg_barrier();
 
   // ---- ping-pong loop: phase ph; group g runs step ph - g ------------------
-  for (int ph = 0; ph <= 2 * T + 1; ++ph) {
+  for (int ph = 0; ph <= 2 * T0 + 1; ++ph) {
     const int step = ph - grp;
     if (step >= 0) {
       if (!(step & 1)) {
@@ -544,6 +569,33 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
       }
     }
     wg_barrier();
+  }
+
+  if constexpr (SPLIT) {
+    // group 1 leaves O, l and its reference in LDS (the rings are no longer
+    // read: the loop ended with a barrier); group 0 merges them into its own
+    constexpr int NW = (D / 32) * 16 + 2;  // floats per lane
+    float *xb = reinterpret_cast<float *>(smem) + (rw * NW) * kWave + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xb[(db * 16 + r) * kWave] = o[db][r];
+      xb[(NW - 2) * kWave] = mbl;
+      xb[(NW - 1) * kWave] = l_run;
+    }
+    wg_barrier();
+    if (grp == 1) return;
+    const float m1 = xb[(NW - 2) * kWave], l1 = xb[(NW - 1) * kWave];
+    const float mm = mbl > m1 ? mbl : m1;  // -inf only if neither half saw a key
+    const float f0 = mbl == neg_inf() ? 0.f : exp2_fast(mbl - mm);
+    const float f1 = m1 == neg_inf() ? 0.f : exp2_fast(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * f0 + xb[(db * 16 + r) * kWave] * f1;
+    l_run = l_run * f0 + l1 * f1;
+    mbl = mm;
   }
 
   // ---- finalise: O / l, lse = scale * m + ln l --------------------------------
@@ -567,19 +619,27 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   }
 }
 
-template <int D, int BN, bool CAUSAL, bool VARLEN>
+template <int D, int BN, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, BN, CAUSAL, VARLEN>), dim3(a.grid), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, BN, CAUSAL, VARLEN, SPLIT>), dim3(a.grid),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int BN>
+template <int D, int BN, bool SPLIT = false>
 hipError_t launch_d(const FwdArgs &a, bool causal, bool varlen, hipStream_t stream) {
   if (causal)
-    return varlen ? launch<D, BN, true, true>(a, stream) : launch<D, BN, true, false>(a, stream);
-  return varlen ? launch<D, BN, false, true>(a, stream) : launch<D, BN, false, false>(a, stream);
+    return varlen ? launch<D, BN, true, true, SPLIT>(a, stream)
+                  : launch<D, BN, true, false, SPLIT>(a, stream);
+  return varlen ? launch<D, BN, false, true, SPLIT>(a, stream)
+                : launch<D, BN, false, false, SPLIT>(a, stream);
 }
+
+// The key-split mode (two LDS rings of 64-key tiles, so d = 64 only) for
+// grids of at most kSplitMaxGrid workgroups of 256 rows, when the longest
+// sequence has at least kSplitMinLen tokens.
+constexpr long long kSplitMaxGrid = 128;
+constexpr int kSplitMinLen = 512;
 
 // Heads of one XCD scheduled together (tile_order): the largest divisor of
 // its head count up to kGroupHeads, so that the 32 CUs of an XCD run about
@@ -604,9 +664,15 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   if (dtype != 1) return hipErrorInvalidValue;
   a.n_qtiles = (a.max_len + kBlockM - 1) / kBlockM;
   a.order_group = head_group(a.batch * a.H);
-  const long long grid = (long long)a.batch * a.H * a.n_qtiles;
+  long long grid = (long long)a.batch * a.H * a.n_qtiles;
+  const bool split = d == 64 && grid <= kSplitMaxGrid && a.max_len >= kSplitMinLen;
+  if (split) {
+    a.n_qtiles = (a.max_len + kBlockM / 2 - 1) / (kBlockM / 2);
+    grid = (long long)a.batch * a.H * a.n_qtiles;
+  }
   if (grid > 0x7fffffffll || grid <= 0) return hipErrorInvalidValue;
   a.grid = (int)grid;
+  if (split) return launch_d<64, 64, true>(a, causal, varlen, stream);
   if (d == 64)
     return a.max_len >= kWideMinLen ? launch_d<64, 128>(a, causal, varlen, stream)
                                     : launch_d<64, 64>(a, causal, varlen, stream);
