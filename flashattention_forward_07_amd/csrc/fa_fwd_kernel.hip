@@ -635,10 +635,15 @@ hipError_t launch_d(const FwdArgs &a, bool causal, bool varlen, hipStream_t stre
                 : launch<D, BN, false, false, SPLIT>(a, stream);
 }
 
-// The key-split mode (two LDS rings of 64-key tiles, so d = 64 only) for
-// grids of at most kSplitMaxGrid workgroups of 256 rows, when the longest
-// sequence has at least kSplitMinLen tokens.
+// The key-split mode (two LDS rings of 64-key tiles, so d = 64 only), when
+// the longest sequence has at least kSplitMinLen tokens and the grid of
+// 256-row workgroups is small: at most 128 workgroups (the split then fills
+// the 256 CUs), or, causal, at most 256 (one round, whose time is the key
+// loop of the heaviest, last query tile).  Measured at d = 64: causal grids
+// of 256 gain 27-37 % from the split and of 512 lose 13-15 %; non-causal
+// grids of 256 lose 20 %.
 constexpr long long kSplitMaxGrid = 128;
+constexpr long long kSplitMaxGridCausal = 256;
 constexpr int kSplitMinLen = 512;
 
 // Heads of one XCD scheduled together (tile_order): the largest divisor of
@@ -665,7 +670,8 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   a.n_qtiles = (a.max_len + kBlockM - 1) / kBlockM;
   a.order_group = head_group(a.batch * a.H);
   long long grid = (long long)a.batch * a.H * a.n_qtiles;
-  const bool split = d == 64 && grid <= kSplitMaxGrid && a.max_len >= kSplitMinLen;
+  const bool split = d == 64 && a.max_len >= kSplitMinLen &&
+                     grid <= (causal ? kSplitMaxGridCausal : kSplitMaxGrid);
   if (split) {
     a.n_qtiles = (a.max_len + kBlockM / 2 - 1) / (kBlockM / 2);
     grid = (long long)a.batch * a.H * a.n_qtiles;

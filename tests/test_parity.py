@@ -294,12 +294,13 @@ def test_varlen_wide_token_rows():
 # --- key range split inside a workgroup (small grids at d = 64) ---------------
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("B,H,N", [(1, 1, 4097), (2, 3, 777), (1, 2, 512)],
-                         ids=["b1h1n4097", "b2h3n777", "b1h2n512"])
+@pytest.mark.parametrize("B,H,N", [(1, 1, 4097), (2, 3, 777), (1, 2, 512), (1, 48, 1000)],
+                         ids=["b1h1n4097", "b2h3n777", "b1h2n512", "b1h48n1000"])
 def test_split_keys_fixed_full(B, H, N, causal):
-    """Grids of at most 128 workgroups of 256 rows at d = 64 (with N >= 512)
-    split each workgroup's key range between its two wave groups and merge
-    the halves; compared in full, outputs NaN-filled beforehand."""
+    """Grids of at most 128 workgroups of 256 rows at d = 64 (256 when
+    causal; N >= 512) split each workgroup's key range between its two wave
+    groups and merge the halves (192 workgroups: split only when causal);
+    compared in full, outputs NaN-filled beforehand."""
     d = 64
     inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=7400 + N + H)
     o, lse = _run_nan_filled(inp, _scale(d), causal, False)
