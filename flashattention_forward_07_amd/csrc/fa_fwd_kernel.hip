@@ -123,7 +123,9 @@ constexpr int kWideMinLen = 256;
 template <int D, int BN_>
 struct Bf16Tile {
   static constexpr int BN = BN_;
-  static_assert(BN == 64 || (BN == 128 && D == 64), "keys per tile");
+  // (32 keys: the key-split mode at d = 128, whose two rings of 64-key tiles
+  // would not fit in LDS)
+  static_assert(BN == 64 || (BN == 128 && D == 64) || (BN == 32 && D == 128), "keys per tile");
   static constexpr int ROWB = D * 2;              // bytes per K/V row
   static constexpr int TILE = BN * ROWB;          // bytes per K (or V) tile
   static constexpr int STAGE = 2 * TILE;          // K tile then V tile
@@ -519,9 +521,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
         m = max3f(m, sc[b][r0 + 5], sc[b][r0 + 6]);
         mq[j] = max2f(m, sc[b][r0 + 7]);
       }
-      float mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
+      float mx;
+      if constexpr (KB == 1) {
+        mx = max2f(mq[0], mq[1]);
+      } else {
+        mx = max2f(max3f(mq[0], mq[1], mq[2]), mq[3]);
 #pragma unroll
-      for (int j = 4; j < 2 * KB; j += 2) mx = max3f(mx, mq[j], mq[j + 1]);
+        for (int j = 4; j < 2 * KB; j += 2) mx = max3f(mx, mq[j], mq[j + 1]);
+      }
       mx = pair_max(mx);
       // rebase when the row grew past the reference, or on its first finite score
       const bool bump = (mbl == neg_inf()) ? (mx > neg_inf()) : (mx > 0.f);
@@ -635,7 +642,8 @@ hipError_t launch_d(const FwdArgs &a, bool causal, bool varlen, hipStream_t stre
                 : launch<D, BN, false, false, SPLIT>(a, stream);
 }
 
-// The key-split mode (two LDS rings of 64-key tiles, so d = 64 only), when
+// The key-split mode (two LDS rings of 4 stages: 64-key tiles at d = 64,
+// 32-key tiles at d = 128), when
 // the longest sequence has at least kSplitMinLen tokens and the grid of
 // 256-row workgroups is small: at most 128 workgroups (the split then fills
 // the 256 CUs), or, causal, at most 256 (one round, whose time is the key
@@ -670,7 +678,7 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   a.n_qtiles = (a.max_len + kBlockM - 1) / kBlockM;
   a.order_group = head_group(a.batch * a.H);
   long long grid = (long long)a.batch * a.H * a.n_qtiles;
-  const bool split = d == 64 && a.max_len >= kSplitMinLen &&
+  const bool split = a.max_len >= kSplitMinLen &&
                      grid <= (causal ? kSplitMaxGridCausal : kSplitMaxGrid);
   if (split) {
     a.n_qtiles = (a.max_len + kBlockM / 2 - 1) / (kBlockM / 2);
@@ -678,7 +686,11 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   }
   if (grid > 0x7fffffffll || grid <= 0) return hipErrorInvalidValue;
   a.grid = (int)grid;
-  if (split) return launch_d<64, 64, true>(a, causal, varlen, stream);
+  if (split) {
+    if (d == 64) return launch_d<64, 64, true>(a, causal, varlen, stream);
+    if (d == 128) return launch_d<128, 32, true>(a, causal, varlen, stream);
+    return hipErrorInvalidValue;
+  }
   if (d == 64)
     return a.max_len >= kWideMinLen ? launch_d<64, 128>(a, causal, varlen, stream)
                                     : launch_d<64, 64>(a, causal, varlen, stream);

@@ -83,7 +83,7 @@ extern "C" {
  * one-tile kernel that computes S, the softmax and P V at once ("Mini
  * FlashAttention", section 3, the one-shot kernel): always for bf16, and for
  * fp32 while the problem is small (N <= 32, or 4 B H N^2 d <= 2^28 flops).
- * bf16 problems at d = 64 with N >= 512 and a small grid (at most 128 query
+ * bf16 problems with N >= 512 and a small grid (at most 128 query
  * tiles of 256 rows, or 256 when causal) split each tile's key range in two
  * halves streamed side by side and merged exactly through their exponent
  * references.  Results meet the same bounds either way.

@@ -293,29 +293,31 @@ def test_varlen_wide_token_rows():
 
 # --- key range split inside a workgroup (small grids at d = 64) ---------------
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,N", [(1, 1, 4097), (2, 3, 777), (1, 2, 512), (1, 48, 1000)],
                          ids=["b1h1n4097", "b2h3n777", "b1h2n512", "b1h48n1000"])
-def test_split_keys_fixed_full(B, H, N, causal):
+def test_split_keys_fixed_full(B, H, N, causal, d):
     """Grids of at most 128 workgroups of 256 rows at d = 64 (256 when
     causal; N >= 512) split each workgroup's key range between its two wave
     groups and merge the halves (192 workgroups: split only when causal);
-    compared in full, outputs NaN-filled beforehand."""
-    d = 64
-    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=7400 + N + H)
+    compared in full, outputs NaN-filled beforehand.  (At d = 128 the split
+    streams 32-key tiles.)"""
+    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=7400 + N + H + d)
     o, lse = _run_nan_filled(inp, _scale(d), causal, False)
     o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, _scale(d), causal)
     gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"split B{B} H{H} N{N}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_split_keys_varlen_full(causal):
+def test_split_keys_varlen_full(causal, d):
     """A packed batch small enough for the key split: ragged lengths, an
     empty sequence and a one-token one."""
-    rng = np.random.default_rng(7500)
+    rng = np.random.default_rng(7500 + d)
     lengths = [1000, 3, 600, 0, 513, 1]
-    inp = fa_inputs.make_varlen(lengths, 2, 64, "bf16", rng)
-    o, lse = _run_nan_filled(inp, _scale(64), causal, True)
-    o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(64),
+    inp = fa_inputs.make_varlen(lengths, 2, d, "bf16", rng)
+    o, lse = _run_nan_filled(inp, _scale(d), causal, True)
+    o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(d),
                                              causal)
     gu.compare(o, o_ref, lse, lse_ref, "bf16", what="split varlen")
