@@ -115,8 +115,9 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o, float *l
                         (dtype == FA_DTYPE_BF16 || N <= 32 || flops <= 268435456.0);
   if (one_tile) {
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const hipError_t e = dtype == FA_DTYPE_BF16 ? fa355::launch_small_bf16(a, d, causal != 0, st)
-                                                : fa355::launch_small_f32(a, d, causal != 0, st);
+    const hipError_t e = dtype == FA_DTYPE_BF16
+                             ? fa355::launch_small_bf16(a, d, causal != 0, false, st)
+                             : fa355::launch_small_f32(a, d, causal != 0, st);
     if (e != hipSuccess) {
       g_last_hip = static_cast<int>(e);
       return FA_ERR_HIP;
@@ -163,6 +164,17 @@ FA_API int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, f
   a.max_len = max_seqlen;
   a.scale = scale;
   a.scale_log2 = scale * kLog2e;
+  // bf16 batches of short sequences (every one a single key tile): the
+  // one-tile kernel, as for fa_fwd
+  if (dtype == FA_DTYPE_BF16 && max_seqlen <= fa355::kSmallMaxN) {
+    const hipError_t e = fa355::launch_small_bf16(a, d, causal != 0, true,
+                                                  reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      g_last_hip = static_cast<int>(e);
+      return FA_ERR_HIP;
+    }
+    return FA_OK;
+  }
   return launch(a, dtype, d, causal, true, stream);
 }
 

@@ -54,30 +54,56 @@ __device__ __forceinline__ u32x2_t tr_read(const uint16_t *p) {
   return __builtin_bit_cast(u32x2_t, x);
 }
 
-template <int D, bool CAUSAL>
+// (sequence, head) pair bh -> its length and element / lse offsets, for a
+// fixed-length batch or (VARLEN) a packed one
+template <bool VARLEN>
+__device__ __forceinline__ void pair_coords(const FwdArgs &a, int bh, int &n, long long &base,
+                                            long long &lbase) {
+  const int s = bh / a.H, hd = bh - s * a.H;
+  if constexpr (VARLEN) {
+    const int t0 = a.cu_seqlens[s];
+    n = a.cu_seqlens[s + 1] - t0;
+    base = (long long)t0 * a.row_stride + (long long)hd * a.head_stride;
+    lbase = (long long)t0 * a.lse_row_stride + (long long)hd * a.lse_head_stride;
+  } else {
+    n = a.n;
+    base = (long long)s * a.seq_stride + (long long)hd * a.head_stride;
+    lbase = (long long)s * a.lse_seq_stride + (long long)hd * a.lse_head_stride;
+  }
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_wg, int nb) {
   constexpr int RSK = D + 8;   // K row stride in LDS (elements): 16-byte pad, conflict-free b128 reads
   constexpr int RSV = D + 16;  // V row stride: 32-byte pad, conflict-free transposing reads
   __shared__ __attribute__((aligned(16))) uint16_t ks[kMaxN * RSK];
   __shared__ __attribute__((aligned(16))) uint16_t vs[kMaxN * RSV];
 
-  const int n = a.n;
   const int n_heads = a.batch * a.H;
   const int h0 = blockIdx.x * heads_per_wg;  // first (sequence, head) of this workgroup
-  const int rows = heads_per_wg * nb;        // staged rows (nb = N rounded up to 32)
+  const int rows = heads_per_wg * nb;        // staged rows (nb = longest N rounded up to 32)
   const uint16_t *kg = static_cast<const uint16_t *>(a.k);
   const uint16_t *vg = static_cast<const uint16_t *>(a.v);
+  // length and offset of each of the (at most 4) heads of the workgroup
+  int sn[4];
+  long long sb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    long long lb;
+    sn[i] = 0;
+    sb[i] = 0;
+    if (i < heads_per_wg && h0 + i < n_heads) pair_coords<VARLEN>(a, h0 + i, sn[i], sb[i], lb);
+  }
 
-  // ---- stage K and V rows of the workgroup's heads (zeros past N) ----
+  // ---- stage K and V rows of the workgroup's heads (zeros past each N) ----
   for (int c = threadIdx.x; c < rows * (D / 8); c += kThreads) {
     const int row = c / (D / 8), col = 8 * (c % (D / 8));
     const int slot = row / nb, key = row - slot * nb;
-    const int bh = h0 + slot;
+    const int n_s = slot == 0 ? sn[0] : slot == 1 ? sn[1] : slot == 2 ? sn[2] : sn[3];
+    const long long b_s = slot == 0 ? sb[0] : slot == 1 ? sb[1] : slot == 2 ? sb[2] : sb[3];
     u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (key < n && bh < n_heads) {
-      const int s = bh / a.H, hd = bh - s * a.H;
-      const long long off = (long long)s * a.seq_stride + (long long)hd * a.head_stride +
-                            (long long)key * a.row_stride + col;
+    if (key < n_s) {  // n_s = 0 for slots past the last head
+      const long long off = b_s + (long long)key * a.row_stride + col;
       kx = *reinterpret_cast<const u32x4_t *>(kg + off);
       vx = *reinterpret_cast<const u32x4_t *>(vg + off);
     }
@@ -93,11 +119,10 @@ __global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_
   const bool active = slot < heads_per_wg && bh < n_heads;  // wave-uniform
   const int qi = 32 * qb + l32;                             // this lane's query
   long long base = 0, lbase = 0;
+  int n = 0;  // this wave's sequence length
   bf16x8_t qr[D / 16];
   if (active) {
-    const int s = bh / a.H, hd = bh - s * a.H;
-    base = (long long)s * a.seq_stride + (long long)hd * a.head_stride;
-    lbase = (long long)s * a.lse_seq_stride + (long long)hd * a.lse_head_stride;
+    pair_coords<VARLEN>(a, bh, n, base, lbase);
     const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
@@ -321,19 +346,19 @@ hipError_t run_f32(const FwdArgs &a, bool causal, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool VARLEN>
 hipError_t run(const FwdArgs &a, bool causal, hipStream_t st) {
-  const int nb = (a.n + 31) & ~31;
+  const int nb = (a.max_len + 31) & ~31;
   const int heads_per_wg = 4 / (nb / 32);  // 4, 2, 1, 1
   const long long n_heads = (long long)a.batch * a.H;
   const long long grid = (n_heads + heads_per_wg - 1) / heads_per_wg;
   if (grid <= 0 || grid > 0x7fffffffll) return hipErrorInvalidValue;
   if (causal)
-    hipLaunchKernelGGL((small_bf16<D, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a,
-                       heads_per_wg, nb);
+    hipLaunchKernelGGL((small_bf16<D, true, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                       a, heads_per_wg, nb);
   else
-    hipLaunchKernelGGL((small_bf16<D, false>), dim3((unsigned)grid), dim3(kThreads), 0, st, a,
-                       heads_per_wg, nb);
+    hipLaunchKernelGGL((small_bf16<D, false, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                       a, heads_per_wg, nb);
   return hipGetLastError();
 }
 
@@ -346,10 +371,12 @@ hipError_t launch_small_f32(const FwdArgs &a, int d, bool causal, hipStream_t st
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, hipStream_t stream) {
-  if (a.n <= 0 || a.n > kSmallMaxN) return hipErrorInvalidValue;
-  if (d == 64) return run<64>(a, causal, stream);
-  if (d == 128) return run<128>(a, causal, stream);
+hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, bool varlen,
+                             hipStream_t stream) {
+  if (a.max_len <= 0 || a.max_len > kSmallMaxN) return hipErrorInvalidValue;
+  if (d == 64) return varlen ? run<64, true>(a, causal, stream) : run<64, false>(a, causal, stream);
+  if (d == 128)
+    return varlen ? run<128, true>(a, causal, stream) : run<128, false>(a, causal, stream);
   return hipErrorInvalidValue;
 }
 

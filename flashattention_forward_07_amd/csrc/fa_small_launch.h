@@ -11,9 +11,12 @@ namespace fa355 {
 // Longest sequence the one-tile kernel takes: one key tile.
 constexpr int kSmallMaxN = 128;
 
-// Fixed-length bf16 batches with 1 <= a.n <= kSmallMaxN (a.batch, a.H, the
-// strides, scale and pointers as for launch_fwd).
-hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, hipStream_t stream);
+// bf16 batches whose longest sequence has 1 <= a.max_len <= kSmallMaxN
+// tokens: fixed-length (a.n = a.max_len) or packed (varlen: lengths from
+// a.cu_seqlens); a.batch, a.H, the strides, scale and pointers as for
+// launch_fwd.
+hipError_t launch_small_bf16(const FwdArgs &a, int d, bool causal, bool varlen,
+                             hipStream_t stream);
 
 // The same for fp32 batches (plain fp32 arithmetic, 16 queries per
 // workgroup).

@@ -321,3 +321,31 @@ def test_split_keys_varlen_full(causal, d):
     o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(d),
                                              causal)
     gu.compare(o, o_ref, lse, lse_ref, "bf16", what="split varlen")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_one_tile_full(causal, d):
+    """Packed bf16 batches whose sequences all fit one key tile (at most 128
+    tokens) take the one-tile kernel: ragged lengths, an empty and a
+    one-token sequence, compared in full."""
+    rng = np.random.default_rng(7600 + d)
+    lengths = [1, 0, 127, 128, 64, 33, 100, 17, 96]
+    inp = fa_inputs.make_varlen(lengths, 3, d, "bf16", rng)
+    o, lse = _run_nan_filled(inp, _scale(d), causal, True)
+    o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(d),
+                                             causal)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what="varlen one-tile")
+
+
+def test_varlen_max_seqlen_above_lengths():
+    """max_seqlen is an upper bound: a looser one (here above the one-tile
+    limit, so the streaming kernel runs) gives the same result."""
+    rng = np.random.default_rng(7700)
+    lengths = [50, 128, 7]
+    inp = fa_inputs.make_varlen(lengths, 2, 64, "bf16", rng)
+    o1, l1 = gu.run_varlen(inp, _scale(64), True)
+    o2, l2 = gu.run_varlen(inp, _scale(64), True, max_seqlen=300)
+    o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, _scale(64), True)
+    gu.compare(o1, o_ref, l1, lse_ref, "bf16", what="one-tile")
+    gu.compare(o2, o_ref, l2, lse_ref, "bf16", what="streaming")
