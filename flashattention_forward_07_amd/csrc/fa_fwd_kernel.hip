@@ -386,6 +386,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   // ---- running state ------------------------------------------------------
   float mbl = neg_inf();    // exponent reference, exp2 domain
   float l_run = 0.f;        // this lane's partial row sum (its half of the keys)
+  float lr_run = 0.f;       // the same over the bf16-rounded weights
   f32x16_t o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
@@ -468,8 +469,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   // above 2^32, so every weight stays <= 2^32.  Otherwise (scores outgrew the
   // reference, or no reference yet) the row max is taken and the reference
   // rebased on it, with O and l rescaled by exp2(old - new).
-  auto weights = [&](float d) {  // P = exp2(x - d) into pb; returns this lane's sum
+  // P = exp2(x - d) into pb.  Returns this lane's sum of the fp32 weights
+  // (for l and lse) and, in *rsum, its sum of the bf16-rounded weights that
+  // the P.V product actually uses (for the division O / l): normalising by
+  // the rounded weights keeps each output row an exact convex combination of
+  // the V rows it uses, so a row dominated by one key returns that key's V
+  // row unchanged whatever the rounding of its weight.
+  auto weights = [&](float d, float *rsum) {
     float pq[4];
+    float rq[2] = {0.f, 0.f};
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int c = 0; c < kBN / 16; ++c)
 #pragma unroll
@@ -483,7 +492,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
           pq[j] = p0 + p1;
         else
           pq[j] += p0 + p1;
+        const bf16x2_t pr = {pb[c][e], pb[c][e + 1]};
+        rq[e >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rq[e >> 2], false);
       }
+    *rsum = rq[0] + rq[1];
     return (pq[0] + pq[1]) + (pq[2] + pq[3]);
   };
   auto v_softmax = [&](int t) {
@@ -504,10 +516,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
           if (!(key < n && (!CAUSAL || key <= qrow))) sc[b][r] = neg_inf();
         }
     }
-    float ps = 0.f, alpha = 1.f;
+    float ps = 0.f, psr = 0.f, alpha = 1.f;
     bool slow = __builtin_amdgcn_ballot_w64(mbl == neg_inf()) != 0;
     if (!slow) {
-      ps = weights(0.f);
+      ps = weights(0.f, &psr);
       slow = __builtin_amdgcn_ballot_w64(!(ps <= FA_FAST_BOUND)) != 0;  // NaN / inf fail too
     }
     if (slow) {
@@ -538,11 +550,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
         alpha = exp2_fast(mbl - mbl_new);  // 0 when there was no reference
         mbl = mbl_new;
       }
-      ps = weights(delta);
+      ps = weights(delta, &psr);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
     l_run = l_run * alpha + ps;
+    lr_run = lr_run * alpha + psr;
   };
   // V(t) also sends tile t + 2 into its LDS stage, whose previous tile t - 2
   // was last read two phases earlier: before the softmax at d = 128, after
@@ -581,13 +594,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
   if constexpr (SPLIT) {
     // group 1 leaves O, l and its reference in LDS (the rings are no longer
     // read: the loop ended with a barrier); group 0 merges them into its own
-    constexpr int NW = (D / 32) * 16 + 2;  // floats per lane
+    constexpr int NW = (D / 32) * 16 + 3;  // floats per lane
     float *xb = reinterpret_cast<float *>(smem) + (rw * NW) * kWave + lane;
     if (grp == 1) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) xb[(db * 16 + r) * kWave] = o[db][r];
+      xb[(NW - 3) * kWave] = lr_run;
       xb[(NW - 2) * kWave] = mbl;
       xb[(NW - 1) * kWave] = l_run;
     }
@@ -602,13 +616,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(const FwdArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * f0 + xb[(db * 16 + r) * kWave] * f1;
     l_run = l_run * f0 + l1 * f1;
+    lr_run = lr_run * f0 + xb[(NW - 3) * kWave] * f1;
     mbl = mm;
   }
 
   // ---- finalise: O / l, lse = scale * m + ln l --------------------------------
+  // (O is divided by the sum of the rounded weights it was built from, lse
+  // takes the fp32 sum)
   const float l_tot = pair_sum(l_run);
+  const float lr_tot = pair_sum(lr_run);
   if (qrow < n) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     uint16_t *orow = reinterpret_cast<uint16_t *>(a.o) + tc.base + (long long)qrow * rs;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

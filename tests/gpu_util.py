@@ -100,6 +100,52 @@ def compare(o_gpu, o_ref, lse_gpu, lse_ref, dtype, what="", max_tol=None):
     return stats
 
 
+class WholeOutput:
+    """Error statistics of a whole output compared chunk by chunk (so that the
+    fp64 reference of a large workload never has to be held at once).  Every
+    element counts: max abs and mean abs of O over the whole output, and the
+    largest relative lse error, against the same bounds as compare()."""
+
+    def __init__(self, dtype, what=""):
+        self.dtype, self.what = dtype, what
+        self.max_abs = 0.0
+        self.sum_abs = 0.0
+        self.count = 0
+        self.lse_rel = 0.0
+        self.rows = 0
+
+    def add(self, o_gpu, o_ref, lse_gpu, lse_ref):
+        o = o_gpu if isinstance(o_gpu, np.ndarray) else host(o_gpu)
+        assert o.shape == o_ref.shape, (o.shape, o_ref.shape)
+        assert np.all(np.isfinite(o)), f"{self.what}: non-finite output (unwritten or NaN)"
+        err = np.abs(o - o_ref)
+        self.max_abs = max(self.max_abs, float(err.max()) if err.size else 0.0)
+        self.sum_abs += float(err.sum())
+        self.count += err.size
+        l = lse_gpu if isinstance(lse_gpu, np.ndarray) else host(lse_gpu)
+        assert l.shape == lse_ref.shape
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(l), fin), f"{self.what}: lse finiteness differs"
+        lerr = np.abs(l[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
+        if lerr.size:
+            self.lse_rel = max(self.lse_rel, float(lerr.max()))
+        self.rows += l.size
+
+    def finish(self, max_tol=None):
+        default_max, mean_tol = TOL[self.dtype]
+        max_tol = default_max if max_tol is None else max_tol
+        mean = self.sum_abs / max(1, self.count)
+        stats = {"rows": self.rows, "elements": self.count, "max_abs": self.max_abs,
+                 "mean_abs": mean, "lse_rel": self.lse_rel}
+        print(f"{self.what}: whole output, {self.rows} rows: max abs {self.max_abs:.3e} "
+              f"mean abs {mean:.3e} lse rel {self.lse_rel:.3e}", flush=True)
+        assert self.max_abs <= max_tol, f"{self.what}: max abs err {self.max_abs:.3e} > {max_tol}"
+        if mean_tol is not None:
+            assert mean <= mean_tol, f"{self.what}: mean abs err {mean:.3e} > {mean_tol}"
+        assert self.lse_rel <= LSE_RTOL, f"{self.what}: lse rel err {self.lse_rel:.3e}"
+        return stats
+
+
 def sample_rows(B, H, N, count, seed, block_m=128, block_n=64):
     """Flat [B, H, N] row indices: every tile edge of a few heads plus random rows."""
     rng = np.random.default_rng(seed)
