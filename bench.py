@@ -37,6 +37,16 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak, B4 H32 N4096 d128 causal, 1 
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+# Vector-ALU work of the method per (query, allowed key) pair, in wave64
+# instruction slots of one SIMD: one exp2 (v_exp_f32), and 2.5 plain fp32 ops
+# (the scale-and-subtract FMA, the row-sum add, half of a two-value bf16
+# pack).  Issue cost per wave64 instruction on one SIMD, measured on MI355X
+# with two waves per SIMD issuing independent streams (see the design notes):
+VALU_CYC_EXP = 8.0
+VALU_CYC_OP = 4.0
+VALU_OPS_PER_PAIR = 2.5
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
 KERNEL_SOURCES = ["flashattention_forward_07_amd/csrc/fa_fwd_kernel.hip",
                   "flashattention_forward_07_amd/csrc/fa_common.h",
                   "flashattention_forward_07_amd/csrc/fa_fwd_launch.h"]
@@ -52,6 +62,79 @@ def attention_flops(lengths, H, d, causal):
     n2 = float(np.sum(np.asarray(lengths, dtype=np.float64) ** 2))
     f = 4.0 * H * n2 * d
     return f / 2.0 if causal else f
+
+
+def attention_pairs(lengths, H, causal):
+    """(query, allowed key) pairs: N^2 per head, N (N + 1) / 2 when causal."""
+    n = np.asarray(lengths, dtype=np.float64)
+    return float(H * np.sum(n * (n + 1) / 2 if causal else n * n))
+
+
+def roofline_terms(flops, pairs, nbytes, kern_s, mfma_peak_tflops):
+    """Lower bounds on the launch time from each unit, and the fraction of
+    the measured launch time each one accounts for:
+      mfma  the metric's flops at the dense matrix-core peak;
+      valu  the softmax's vector work (one exp2 and VALU_OPS_PER_PAIR plain
+            ops per pair, 64 lanes per instruction) at the measured issue
+            costs, on all SIMDs at the 2.4 GHz peak clock;
+      hbm   the compulsory bytes at 8 TB/s.
+    The binding term is the largest bound."""
+    t_mfma = flops / (mfma_peak_tflops * 1e12)
+    t_valu = pairs / 64.0 * (VALU_CYC_EXP + VALU_OPS_PER_PAIR * VALU_CYC_OP) / (SIMDS * CLOCK_HZ)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    terms = {"mfma_us": t_mfma * 1e6, "valu_us": t_valu * 1e6, "hbm_us": t_hbm * 1e6}
+    out = {k: round(v, 3) for k, v in terms.items()}
+    out.update({"mfma_frac": round(t_mfma / kern_s, 4), "valu_frac": round(t_valu / kern_s, 4),
+                "hbm_frac": round(t_hbm / kern_s, 4)})
+    out["binding"] = max(("mfma", t_mfma), ("valu", t_valu), ("hbm", t_hbm), key=lambda x: x[1])[0]
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def prewarm(torch, step, seconds):
+    """Untimed launches for a fixed wall time, so the timed steps start from
+    the clock and power state the GPU holds under sustained load (a fresh
+    GPU's first tens of milliseconds of launches run slower)."""
+    if seconds <= 0:
+        return 0, 0.0
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n, el
+
+
+def cold_cache_us(torch, step, reps, flush_bytes=1 << 30):
+    """Median launch time with the caches flushed before every launch: a
+    1 GiB buffer (larger than the L2s and the Infinity Cache together) is
+    overwritten between launches, outside the timed events."""
+    st = torch.cuda.current_stream()
+    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(reps):
+        junk.fill_(float(i))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        step()
+        b.record(st)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    del junk
+    return float(np.median(times))
 
 
 def algorithmic_bytes(total_tokens, H, d, elem):
@@ -245,7 +328,7 @@ def bench_decode(args, torch, fa):
         dt = time.perf_counter() - t0
         cb = n * nbytes / w.B
         result["cpu_baseline"] = {"value": round(cb / dt / 1e9, 3), "unit": "GB/s",
-                                  "cores": threads, "kind": "oracle",
+                                  "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
                                   "sample": f"{n} of {w.B} batch entries (all {w.H} heads each) "
                                             f"in {dt:.1f} s, fp64"}
         log(f"[bench] cpu baseline {result['cpu_baseline']}")
@@ -375,6 +458,9 @@ def main():
                     help="a prefill workload (fa_fwd), or a decode_* workload (fa_decode_fwd, "
                          "split-KV, measured in GB/s against the HBM peak)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm-s", type=float, default=2.0,
+                    help="seconds of untimed launches before the warm-up steps (reported as "
+                         "prewarm_s; 0 disables)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     ap.add_argument("--method", choices=["fused", "naive"], default="fused",
                     help="fused: fa_fwd (the library's kernel); naive: fa_naive_fwd, the "
@@ -469,6 +555,8 @@ def main():
         alg_bytes = naive_bytes(w.N, w.B, w.H, w.d, elem, w.causal)
 
     stream = torch.cuda.current_stream()  # fa_fwd launches on this stream
+    n_pre, t_pre = prewarm(torch, step, args.prewarm_s)
+    log(f"[bench] prewarm: {n_pre} untimed launches in {t_pre:.2f} s")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -487,8 +575,12 @@ def main():
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kern_ms = float(np.mean(per_launch_ms))
     ms_per_step = wall * 1e3 / args.steps
+    qn = max(1, len(per_launch_ms) // 4)
+    q1_ms = float(np.mean(per_launch_ms[:qn]))
+    q4_ms = float(np.mean(per_launch_ms[-qn:]))
     log(f"[bench] kernel mean {kern_ms:.4f} ms, median {np.median(per_launch_ms):.4f} ms, "
-        f"min {np.min(per_launch_ms):.4f} ms; wall {ms_per_step:.4f} ms/step")
+        f"min {np.min(per_launch_ms):.4f} ms; first quarter {q1_ms:.4f} ms, last quarter "
+        f"{q4_ms:.4f} ms; wall {ms_per_step:.4f} ms/step")
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)  # 1 GiB
@@ -502,6 +594,9 @@ def main():
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     traffic = committed_traffic(w.name) if args.method == "fused" else None
+    pairs = attention_pairs(lengths, w.H, w.causal)
+    terms = roofline_terms(flops, pairs, alg_bytes, kern_ms * 1e-3, peak)
+    log(f"[bench] roofline terms {terms}")
     log(f"[bench] {value:.1f} TFLOP/s per step, kernel {achieved:.1f} TFLOP/s = "
         f"{100 * achieved / peak:.1f}% of {peak:.1f}; algorithmic bytes {alg_bytes / 1e6:.1f} MB "
         f"-> {alg_bytes / (kern_ms * 1e-3) / 1e9:.0f} GB/s")
@@ -530,8 +625,36 @@ def main():
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "terms": terms},
+        "launch_ms": {"mean": round(kern_ms, 5), "median": round(float(np.median(per_launch_ms)), 5),
+                      "min": round(float(np.min(per_launch_ms)), 5),
+                      "first_quarter": round(q1_ms, 5), "last_quarter": round(q4_ms, 5)},
+        "prewarm_s": round(t_pre, 3),
+        "prewarm_launches": n_pre,
     }
+    if terms["binding"] == "valu" and args.method == "fused":
+        # the softmax's vector work bounds this workload (d = 64: half the
+        # matrix work per exp2); report the fraction against that unit, in
+        # (query, key) pairs per second, and keep the matrix-core fraction
+        vpeak = pairs / (terms["valu_us"] * 1e-6) / 1e9
+        vach = pairs / (kern_ms * 1e-3) / 1e9
+        result["roofline"].update({"bound": "alu", "achieved": round(vach, 1),
+                                   "peak": round(vpeak, 1), "unit": "Gpair/s",
+                                   "frac": round(vach / vpeak, 4),
+                                   "mfma_achieved_tflops": round(achieved, 3),
+                                   "mfma_frac": round(achieved / peak, 4)})
+    elif terms["binding"] == "hbm" and args.method == "fused":
+        gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+        result["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1),
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                   "mfma_achieved_tflops": round(achieved, 3),
+                                   "mfma_frac": round(achieved / peak, 4)})
+    if alg_bytes <= (64 << 20) and args.method == "fused":
+        # small workloads: also the launch with cold caches
+        cc = cold_cache_us(torch, step, reps=max(10, min(args.steps, 50)))
+        result["cold_cache_us"] = round(cc, 2)
+        log(f"[bench] cold caches: median {cc:.2f} us per launch")
     if args.method == "naive":
         # three launches per step, bound by the N x N round trips through HBM
         gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
@@ -541,6 +664,7 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on the host (~{args.cpu_budget:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
         log(f"[bench] cpu baseline {result['cpu_baseline']}")
     else:
         result["cpu_baseline"] = None
