@@ -22,6 +22,7 @@ __all__ = [
     "fa_status_string", "fa_last_hip_error", "fa_version", "attention",
     "attention_varlen", "library_path", "load", "fa_naive_fwd", "fa_naive_workspace_bytes",
     "naive_attention", "fa_decode_fwd", "fa_decode_workspace_bytes", "fa_decode_num_splits",
+    "fa_decode_fwd_noalloc", "FA_DECODE_SCRATCH_BYTES",
     "decode_attention",
 ]
 
@@ -71,6 +72,9 @@ def load():
     lib.fa_decode_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, i32, i32, i32, i32, i32,
                                   f32, i32, i32, i32, P]
     lib.fa_decode_fwd.restype = i32
+    lib.fa_decode_fwd_noalloc.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32,
+                                          i32, P]
+    lib.fa_decode_fwd_noalloc.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode_num_splits.argtypes = [i32, i32, i32, i32, i32]
@@ -160,6 +164,22 @@ def fa_decode_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, d, 
                               _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_decode_fwd")
+
+
+# Size of the library's static decode scratch (FA_DECODE_SCRATCH_BYTES).
+FA_DECODE_SCRATCH_BYTES = 16 << 20
+
+
+def fa_decode_fwd_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits=0,
+                          stream=None) -> None:
+    """Enqueue the split-KV decode forward with its partial results in the
+    library's static per-GPU scratch (no workspace, no allocation)."""
+    st = load().fa_decode_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
+                                      int(H), int(Nq), int(Nk), int(d), float(scale),
+                                      int(bool(causal)), int(dtype), int(num_splits),
+                                      _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_fwd_noalloc")
 
 
 def fa_status_string(status: int) -> str:

@@ -5,6 +5,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "fa355.h"
@@ -56,6 +59,172 @@ int launch(const fa355::FwdArgs &a, int dtype, int d, int causal, bool varlen, v
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+// Split plan of fa_decode_fwd: key ranges of `chunk` keys (a multiple of
+// 16), `splits` of them per (b, h), and `qchunks` groups of queries.  With
+// num_splits = 0 the ranges are sized for about one streaming wave per SIMD
+// (1024 waves), or two when a wave carries 4 queries and has more arithmetic
+// per byte to hide; fewer, longer streams measured faster than more, shorter
+// ones.  No range is shorter than 256 keys.  A request is capped at Nk, and
+// rounding the range up to 16 keys can lower it further.
+namespace {
+constexpr int kDecodeMaxQ = 64;
+constexpr int kDecodeMinKeys = 256;
+
+struct DecodePlan {
+  bool ok;
+  int splits, chunk, qchunks;
+  long long tasks;
+  size_t ws_bytes;  // 0 when splits == 1
+};
+
+DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  DecodePlan p{};
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || Nq > kDecodeMaxQ || num_splits < 0) return p;
+  if (d != 64 && d != 128) return p;
+  const long long bh = (long long)B * H;
+  if (Nk > (1 << 30) || bh * (Nq > Nk ? Nq : Nk) > kMaxRows) return p;
+  if (bh * Nq * d / 256 > kMaxGrid) return p;  // merge grid
+  const int nqw = fa355::decode_queries_per_wave(Nq);
+  p.qchunks = (Nq + nqw - 1) / nqw;
+  const long long items = bh * p.qchunks;
+  long long req = num_splits;
+  if (req == 0) {
+    const long long target = nqw >= 4 ? 2048 : 1024;
+    req = (target + items - 1) / items;
+    const long long cap = Nk / kDecodeMinKeys > 1 ? Nk / kDecodeMinKeys : 1;
+    if (req > cap) req = cap;
+  }
+  if (req > Nk) req = Nk;
+  long long chunk = (Nk + req - 1) / req;
+  chunk = (chunk + 15) & ~15ll;
+  p.chunk = static_cast<int>(chunk);
+  p.splits = static_cast<int>((Nk + chunk - 1) / chunk);
+  p.tasks = items * p.splits;
+  if (p.tasks > 4 * kMaxGrid) return p;
+  const unsigned long long rows = (unsigned long long)bh * Nq;
+  p.ws_bytes = p.splits > 1 ? (size_t)(p.splits * rows * (unsigned long long)(d + 1) * 4ull) : 0;
+  p.ok = true;
+  return p;
+}
+}  // namespace
+
+// ---- static scratch of fa_decode_fwd_noalloc ------------------------------
+// The split partial results of fa_decode_fwd_noalloc live in this array: one
+// copy per GPU, created with the code object when the library is loaded on
+// that GPU and held until the process ends.  Host code never uses the name
+// itself as an address (on the host it is only a stand-in for the symbol):
+// each GPU's copy is looked up once, with that GPU current, by
+// hipGetSymbolAddress, and that address is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Address of the current GPU's scratch array, looked up on the first call
+// made with that GPU current; nullptr (with *status set) on failure.
+void *device_scratch(int *status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip = static_cast<int>(e);
+    *status = FA_ERR_HIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_hip = static_cast<int>(hipErrorInvalidDevice);
+    *status = FA_ERR_HIP;
+    return nullptr;
+  }
+  void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch[dev].load(std::memory_order_relaxed);
+  if (ptr == nullptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      g_last_hip = static_cast<int>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      *status = FA_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+// fa_decode_fwd and fa_decode_fwd_noalloc: the same validation, plan and
+// kernels; the partial results go to the caller's workspace, or (noalloc) to
+// the current GPU's static scratch array.
+int decode_common(const void *q, const void *k, const void *v, void *o, float *lse,
+                  void *workspace, size_t workspace_bytes, bool noalloc, int B, int H, int Nq,
+                  int Nk, int d, float scale, int causal, int dtype, int num_splits,
+                  void *stream) {
+  int st = value_checks(d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || num_splits < 0) return FA_ERR_SHAPE;
+  if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+  const DecodePlan p = decode_plan(B, H, Nq, Nk, d, num_splits);
+  if (!p.ok) return FA_ERR_SHAPE;
+  st = pointer_checks(q, k, v, o, lse);
+  if (st != FA_OK) return st;
+  if (p.ws_bytes > 0 && noalloc) {
+    if (p.ws_bytes > FA_DECODE_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  } else if (p.ws_bytes > 0) {
+    if (!workspace) return FA_ERR_NULL;
+    if (misaligned(workspace, 16)) return FA_ERR_ALIGN;
+    if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+  }
+  const long long bh = (long long)B * H;
+  const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  const size_t qbytes = (size_t)(bh * Nq) * d * esz, kbytes = (size_t)(bh * Nk) * d * esz;
+  const size_t lbytes = (size_t)(bh * Nq) * sizeof(float);
+  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
+      overlap(o, qbytes, v, kbytes))
+    return FA_ERR_ALIAS;
+  if (lse && (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+              overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes)))
+    return FA_ERR_ALIAS;
+  if (p.ws_bytes > 0 && !noalloc &&
+      (overlap(workspace, p.ws_bytes, q, qbytes) || overlap(workspace, p.ws_bytes, k, kbytes) ||
+       overlap(workspace, p.ws_bytes, v, kbytes) || overlap(workspace, p.ws_bytes, o, qbytes) ||
+       (lse && overlap(workspace, p.ws_bytes, lse, lbytes))))
+    return FA_ERR_ALIAS;
+  if (p.ws_bytes > 0 && noalloc) {  // every argument check has passed
+    workspace = device_scratch(&st);
+    if (!workspace) return st;
+  }
+  fa355::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  if (p.ws_bytes > 0) {
+    a.part_o = static_cast<float *>(workspace);
+    a.part_lse = a.part_o + (size_t)p.splits * (size_t)(bh * Nq) * d;
+  }
+  a.bh = bh;
+  a.nq = Nq;
+  a.nk = Nk;
+  a.splits = p.splits;
+  a.chunk = p.chunk;
+  a.qchunks = p.qchunks;
+  a.tasks = p.tasks;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  const hipError_t e = fa355::launch_decode(a, dtype, d, causal != 0,
+                                            reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
 
 }  // namespace
 
@@ -239,54 +408,6 @@ FA_API int fa_naive_fwd(const void *q, const void *k, const void *v, void *o, fl
   return FA_OK;
 }
 
-// Split plan of fa_decode_fwd: key ranges of `chunk` keys (a multiple of
-// 16), `splits` of them per (b, h), and `qchunks` groups of queries.  With
-// num_splits = 0 the ranges are sized for about one streaming wave per SIMD
-// (1024 waves), or two when a wave carries 4 queries and has more arithmetic
-// per byte to hide; fewer, longer streams measured faster than more, shorter
-// ones.  No range is shorter than 256 keys.  A request is capped at Nk, and
-// rounding the range up to 16 keys can lower it further.
-namespace {
-constexpr int kDecodeMaxQ = 64;
-constexpr int kDecodeMinKeys = 256;
-
-struct DecodePlan {
-  bool ok;
-  int splits, chunk, qchunks;
-  long long tasks;
-  size_t ws_bytes;  // 0 when splits == 1
-};
-
-DecodePlan decode_plan(int B, int H, int Nq, int Nk, int d, int num_splits) {
-  DecodePlan p{};
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || Nq > kDecodeMaxQ || num_splits < 0) return p;
-  if (d != 64 && d != 128) return p;
-  const long long bh = (long long)B * H;
-  if (Nk > (1 << 30) || bh * (Nq > Nk ? Nq : Nk) > kMaxRows) return p;
-  if (bh * Nq * d / 256 > kMaxGrid) return p;  // merge grid
-  const int nqw = fa355::decode_queries_per_wave(Nq);
-  p.qchunks = (Nq + nqw - 1) / nqw;
-  const long long items = bh * p.qchunks;
-  long long req = num_splits;
-  if (req == 0) {
-    const long long target = nqw >= 4 ? 2048 : 1024;
-    req = (target + items - 1) / items;
-    const long long cap = Nk / kDecodeMinKeys > 1 ? Nk / kDecodeMinKeys : 1;
-    if (req > cap) req = cap;
-  }
-  if (req > Nk) req = Nk;
-  long long chunk = (Nk + req - 1) / req;
-  chunk = (chunk + 15) & ~15ll;
-  p.chunk = static_cast<int>(chunk);
-  p.splits = static_cast<int>((Nk + chunk - 1) / chunk);
-  p.tasks = items * p.splits;
-  if (p.tasks > 4 * kMaxGrid) return p;
-  const unsigned long long rows = (unsigned long long)bh * Nq;
-  p.ws_bytes = p.splits > 1 ? (size_t)(p.splits * rows * (unsigned long long)(d + 1) * 4ull) : 0;
-  p.ok = true;
-  return p;
-}
-}  // namespace
 
 FA_API size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
   const DecodePlan p = decode_plan(B, H, Nq, Nk, d, num_splits);
@@ -301,60 +422,15 @@ FA_API int fa_decode_num_splits(int B, int H, int Nq, int Nk, int num_splits) {
 FA_API int fa_decode_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                          void *workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk,
                          int d, float scale, int causal, int dtype, int num_splits, void *stream) {
-  int st = value_checks(d, scale, dtype);
-  if (st != FA_OK) return st;
-  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || num_splits < 0) return FA_ERR_SHAPE;
-  if (B == 0 || H == 0 || Nq == 0) return FA_OK;
-  const DecodePlan p = decode_plan(B, H, Nq, Nk, d, num_splits);
-  if (!p.ok) return FA_ERR_SHAPE;
-  st = pointer_checks(q, k, v, o, lse);
-  if (st != FA_OK) return st;
-  if (p.ws_bytes > 0) {
-    if (!workspace) return FA_ERR_NULL;
-    if (misaligned(workspace, 16)) return FA_ERR_ALIGN;
-    if (workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
-  }
-  const long long bh = (long long)B * H;
-  const size_t esz = dtype == FA_DTYPE_BF16 ? 2 : 4;
-  const size_t qbytes = (size_t)(bh * Nq) * d * esz, kbytes = (size_t)(bh * Nk) * d * esz;
-  const size_t lbytes = (size_t)(bh * Nq) * sizeof(float);
-  if (overlap(o, qbytes, q, qbytes) || overlap(o, qbytes, k, kbytes) ||
-      overlap(o, qbytes, v, kbytes))
-    return FA_ERR_ALIAS;
-  if (lse && (overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
-              overlap(lse, lbytes, v, kbytes) || overlap(lse, lbytes, o, qbytes)))
-    return FA_ERR_ALIAS;
-  if (p.ws_bytes > 0 &&
-      (overlap(workspace, p.ws_bytes, q, qbytes) || overlap(workspace, p.ws_bytes, k, kbytes) ||
-       overlap(workspace, p.ws_bytes, v, kbytes) || overlap(workspace, p.ws_bytes, o, qbytes) ||
-       (lse && overlap(workspace, p.ws_bytes, lse, lbytes))))
-    return FA_ERR_ALIAS;
-  fa355::DecodeArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  if (p.ws_bytes > 0) {
-    a.part_o = static_cast<float *>(workspace);
-    a.part_lse = a.part_o + (size_t)p.splits * (size_t)(bh * Nq) * d;
-  }
-  a.bh = bh;
-  a.nq = Nq;
-  a.nk = Nk;
-  a.splits = p.splits;
-  a.chunk = p.chunk;
-  a.qchunks = p.qchunks;
-  a.tasks = p.tasks;
-  a.scale = scale;
-  a.scale_log2 = scale * kLog2e;
-  const hipError_t e = fa355::launch_decode(a, dtype, d, causal != 0,
-                                            reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip = static_cast<int>(e);
-    return FA_ERR_HIP;
-  }
-  return FA_OK;
+  return decode_common(q, k, v, o, lse, workspace, workspace_bytes, false, B, H, Nq, Nk, d, scale,
+                       causal, dtype, num_splits, stream);
+}
+
+FA_API int fa_decode_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                                 int dtype, int num_splits, void *stream) {
+  return decode_common(q, k, v, o, lse, nullptr, 0, true, B, H, Nq, Nk, d, scale, causal, dtype,
+                       num_splits, stream);
 }
 
 FA_API const char *fa_status_string(int status) {
@@ -370,6 +446,8 @@ FA_API const char *fa_status_string(int status) {
     case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed (see fa_last_hip_error)";
     case FA_ERR_WORKSPACE:
       return "FA_ERR_WORKSPACE: workspace smaller than the entry point's *_workspace_bytes()";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the split partial results exceed FA_DECODE_SCRATCH_BYTES";
     default: return "unknown status";
   }
 }

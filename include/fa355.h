@@ -64,6 +64,7 @@ extern "C" {
 #define FA_ERR_ALIAS 7    /* an output overlaps an input or the other output */
 #define FA_ERR_HIP 8      /* the HIP launch failed; see fa_last_hip_error() */
 #define FA_ERR_WORKSPACE 9 /* workspace smaller than the *_workspace_bytes() size */
+#define FA_ERR_SCRATCH 10  /* fa_decode_fwd_noalloc: partials exceed the static scratch */
 
 /*
  * fa_fwd -- attention forward over a fixed-length batch.
@@ -187,6 +188,31 @@ FA_API int fa_decode_fwd(const void *q, const void *k, const void *v, void *o,
                          float *lse, void *workspace, size_t workspace_bytes,
                          int B, int H, int Nq, int Nk, int d, float scale,
                          int causal, int dtype, int num_splits, void *stream);
+
+/*
+ * fa_decode_fwd_noalloc -- fa_decode_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the
+ * same split plan, kernels and results.  The split partial results go to a
+ * static device array of FA_DECODE_SCRATCH_BYTES inside the library, one
+ * copy per GPU, held until the process ends; the call uses the copy of the
+ * current device (hipGetDevice), so `stream` must belong to that device.
+ * The call itself allocates nothing (no hipMalloc, no library allocator).
+ *
+ * Problems whose partial results, fa_decode_workspace_bytes(B, H, Nq, Nk,
+ * d, num_splits), exceed FA_DECODE_SCRATCH_BYTES return FA_ERR_SCRATCH and
+ * enqueue nothing; pass a smaller num_splits, or use fa_decode_fwd with a
+ * workspace.  Every call on one GPU shares that GPU's array and overwrites
+ * it (nothing in it needs to start at zero): calls whose kernels may run
+ * at the same time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  The first call on a device looks up
+ * the array's address (FA_ERR_HIP if that fails).
+ */
+#define FA_DECODE_SCRATCH_BYTES (16u << 20)
+FA_API int fa_decode_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 void *o, float *lse, int B, int H, int Nq,
+                                 int Nk, int d, float scale, int causal,
+                                 int dtype, int num_splits, void *stream);
 
 /* Workspace bytes fa_decode_fwd needs for these sizes: splits x B H Nq x
  * (d + 1) floats when the keys are split, else 0; also 0 when the sizes are

@@ -37,6 +37,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert set(_declared()) == {"fa_fwd", "fa_fwd_varlen", "fa_naive_fwd",
                                 "fa_naive_workspace_bytes", "fa_decode_fwd",
+                                "fa_decode_fwd_noalloc",
                                 "fa_decode_workspace_bytes", "fa_decode_num_splits",
                                 "fa_status_string", "fa_last_hip_error", "fa_version"}
 
@@ -207,6 +208,33 @@ def test_decode_rejects_bad_arguments(lib):
     # empty problems are a no-op; one key range needs no workspace
     assert _decode(lib, B=0, ws=None) == 0 and _decode(lib, Nq=0, ws=None) == 0
     assert lib.fa_decode_workspace_bytes(1, 1, 1, 64, 64, 1) == 0
+
+
+def _decode_noalloc(lib, q=A, k=A + S, v=A + 2 * S, o=A + 3 * S, lse=None, B=1, H=1, Nq=1,
+                    Nk=64, d=64, scale=0.125, causal=0, dtype=BF16, splits=2):
+    return lib.fa_decode_fwd_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, ctypes.c_float(scale),
+                                     causal, dtype, splits, None)
+
+
+def test_decode_noalloc_rejects_bad_arguments(lib):
+    c = _status_codes()
+    text = open(HEADER).read()
+    limit = re.search(r"#define FA_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert limit and int(limit[1]) << int(limit[2]) == fa.FA_DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(lib, v=None) == c["FA_ERR_NULL"]
+    assert _decode_noalloc(lib, q=A + 8) == c["FA_ERR_ALIGN"]
+    assert _decode_noalloc(lib, d=32) == c["FA_ERR_HEAD_DIM"]
+    assert _decode_noalloc(lib, dtype=3) == c["FA_ERR_DTYPE"]
+    assert _decode_noalloc(lib, scale=0.0) == c["FA_ERR_SCALE"]
+    assert _decode_noalloc(lib, Nq=65) == c["FA_ERR_SHAPE"]
+    assert _decode_noalloc(lib, o=A) == c["FA_ERR_ALIAS"]
+    # partials beyond the static scratch: rejected before anything else runs
+    B, H, Nq, Nk, d, sp = 64, 32, 8, 1 << 20, 128, 8
+    need = lib.fa_decode_workspace_bytes(B, H, Nq, Nk, d, sp)
+    assert need > fa.FA_DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(lib, B=B, H=H, Nq=Nq, Nk=Nk, d=d, splits=sp) == c["FA_ERR_SCRATCH"]
+    # empty problems are a no-op
+    assert _decode_noalloc(lib, B=0) == 0 and _decode_noalloc(lib, Nq=0) == 0
 
 
 def test_python_binding_raises_on_error(lib):
