@@ -46,6 +46,10 @@ constexpr int kMinBlockM = 128;
 hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
                       hipStream_t stream);
 
+// The pipelined bf16 kernel at d = 128 (fa_fwd_pipe.hip): 256 query rows per
+// workgroup, like the 8-wave kernel, so the same grid and tile order.
+hipError_t launch_fwd_pipe(const FwdArgs &a, bool causal, bool varlen, hipStream_t stream);
+
 // The fp32 kernel (fa_fwd_f32.hip).
 hipError_t launch_fwd_f32(FwdArgs a, int d, bool causal, bool varlen, hipStream_t stream);
 

@@ -52,15 +52,20 @@ def test_small_shapes_full(dtype, d, causal, shape):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_wide_score_range(dtype):
-    # Q and K x8: scores spread over hundreds, the max moves across tiles.
-    inp = fa_inputs.make_fixed(1, 2, 333, 128, dtype, seed=77, qk_mult=8.0)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [333, 1000])
+def test_wide_score_range(dtype, d, N):
+    # Q and K x8: scores spread over hundreds, the max moves across tiles and
+    # the running reference is rebased on many of them, with rows of one
+    # wave rebasing by very different factors.
+    inp = fa_inputs.make_fixed(1, 4, N, d, dtype, seed=77 + N, qk_mult=8.0)
     for causal in (False, True):
-        o, lse = gu.run_fixed(inp, _scale(128), causal)
-        o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, _scale(128), causal)
+        o, lse = gu.run_fixed(inp, _scale(d), causal)
+        o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, _scale(d), causal)
         # fp32: scores of |q.k| ~ 1e3 carry fp32 rounding far above 1e-5
-        tol = gu.fp32_score_tol(inp.q, inp.k, inp.v, _scale(128)) if dtype == "f32" else None
-        gu.compare(o, o_ref, lse, lse_ref, dtype, what=f"x8 causal={causal}", max_tol=tol)
+        tol = gu.fp32_score_tol(inp.q, inp.k, inp.v, _scale(d)) if dtype == "f32" else None
+        gu.compare(o, o_ref, lse, lse_ref, dtype, what=f"x8 d={d} N={N} causal={causal}",
+                   max_tol=tol)
 
 
 # --- the five named workloads at full size ----------------------------------
