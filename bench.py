@@ -48,6 +48,8 @@ VALU_OPS_PER_PAIR = 2.5
 SIMDS = 256 * 4
 CLOCK_HZ = 2.4e9
 KERNEL_SOURCES = ["flashattention_forward_07_amd/csrc/fa_fwd_kernel.hip",
+                  "flashattention_forward_07_amd/csrc/fa_fwd_pipe.hip",
+                  "flashattention_forward_07_amd/csrc/fa_bf16_tile.h",
                   "flashattention_forward_07_amd/csrc/fa_common.h",
                   "flashattention_forward_07_amd/csrc/fa_fwd_launch.h"]
 

@@ -348,6 +348,40 @@ struct BodySchedule {
 #define FA_PIPE_READ_AHEAD 6
 #endif
 constexpr int kPReadAhead = FA_PIPE_READ_AHEAD;
+// Operand waits of a body, per slot (-1: none).  A product that first reads
+// an operand waits for its reads; each such wait also covers the operands of
+// the next kPWaitGroup - 1 owners whose reads have gone out by then (they
+// went out kPReadAhead slots ahead of their own products), so one s_waitcnt
+// serves several operands.  The reads issued before slot k's product are
+// those of the slots before k + kPReadAhead.
+#ifndef FA_PIPE_WAIT_GROUP
+#define FA_PIPE_WAIT_GROUP 2
+#endif
+constexpr int kPWaitGroup = FA_PIPE_WAIT_GROUP;
+template <bool PV, bool S>
+struct BodyWaits {
+  static constexpr int N = BodySchedule<PV, S>::N;
+  int w[N];
+  constexpr BodyWaits() : w{} {
+    constexpr BodySchedule<PV, S> bs{};
+    int owners[N] = {};
+    int no = 0;
+    for (int k = 0; k < N; ++k) {
+      w[k] = -1;
+      if (bs.slot[k].reads > 0) owners[no++] = k;
+    }
+    for (int o = 0; o < no;) {
+      const int k = owners[o];
+      const int hi = k + kPReadAhead < N ? k + kPReadAhead : N;
+      int g = 1;
+      while (g < kPWaitGroup && o + g < no && owners[o + g] < hi) ++g;
+      const int covered = owners[o + g - 1];
+      w[k] = bs.reads_before[hi] - bs.reads_before[covered + 1];
+      o += g;
+    }
+  }
+};
+
 // Ring entries for the operands of one kind: an operand is live from its
 // reads (issued behind the product kPReadAhead slots before its first use)
 // until its second use one slot after the first, so at most the owners of
@@ -650,6 +684,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
                    SM = decltype(sm_c)::value;
     constexpr int SB = decltype(sb_c)::value;  // S(t) in set SB, S(t+1) goes to set 1 - SB
     constexpr BodySchedule<PV, S> BS{};
+    constexpr BodyWaits<PV, S> BW{};
     constexpr int N = BS.N;
     static_assert(!SM || (PV && S), "the softmax runs in full bodies only");
     constexpr int NRV = ring_size<PV, S>(0), NRK = ring_size<PV, S>(2);
@@ -690,18 +725,14 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
       constexpr int k = decltype(K)::value;
       constexpr Slot sl = BS.slot[k];
       auto &y = pick<sl.blk>(A, B);
-      // the reads of slots k+1 .. k+RA-1 may stay in flight (slot k+RA's go
-      // out right behind this slot's product)
-      constexpr int last = (k + RA - 1 < N) ? k + RA - 1 : N - 1;
-      constexpr int in_flight = BS.reads_before[last + 1] - BS.reads_before[k + 1];
+      constexpr int W = BW.w[k];  // operand wait (-1: none, see BodyWaits)
       if constexpr (sl.kind == 0) {
-        mfma_pv<sl.blk, sl.x, sl.op % NRV, (sl.reads > 0 ? in_flight : -1)>(
-            y.o[sl.x], vr[sl.op % NRV], y.p[sl.c]);
+        mfma_pv<sl.blk, sl.x, sl.op % NRV, W>(y.o[sl.x], vr[sl.op % NRV], y.p[sl.c]);
       } else if constexpr (sl.kind == 1) {
         mfma_ones(y.lr, ones, y.p[sl.c]);
       } else {
-        mfma_s<sl.blk, sl.c, sl.c == 0, sl.op % NRK, (sl.reads > 0 ? in_flight : -1)>(
-            y.s[1 - SB][sl.x], kr[sl.op % NRK], y.q[sl.c]);
+        mfma_s<sl.blk, sl.c, sl.c == 0, sl.op % NRK, W>(y.s[1 - SB][sl.x], kr[sl.op % NRK],
+                                                        y.q[sl.c]);
       }
       // LDS reads issue right behind a product: there they cost nothing,
       // while behind the slot's vector work they hold up the next product
@@ -747,12 +778,12 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
           if constexpr (sm_fma(u) == k) {
             x.s[SB][kb][r] = __builtin_fmaf(x.s[SB][kb][r], sl2, -x.g);
             x.s[SB][kb][r + 1] = __builtin_fmaf(x.s[SB][kb][r + 1], sl2, -x.g);
-            asm volatile("" : "+v"(x.s[SB][kb][r]), "+v"(x.s[SB][kb][r + 1]));
+            asm volatile("" ::"v"(x.s[SB][kb][r]), "v"(x.s[SB][kb][r + 1]));
           }
           if constexpr (sm_exp(u) == k) {
             x.s[SB][kb][r] = exp2_fast(x.s[SB][kb][r]);
             x.s[SB][kb][r + 1] = exp2_fast(x.s[SB][kb][r + 1]);
-            asm volatile("" : "+v"(x.s[SB][kb][r]), "+v"(x.s[SB][kb][r + 1]));
+            asm volatile("" ::"v"(x.s[SB][kb][r]), "v"(x.s[SB][kb][r + 1]));
           }
           if constexpr (sm_pack(u) == k) {
             x.p[c][e] = (__bf16)x.s[SB][kb][r];
@@ -762,7 +793,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
               ps[bi][i] = x.s[SB][kb][r] + x.s[SB][kb][r + 1];
             else
               ps[bi][i] += x.s[SB][kb][r] + x.s[SB][kb][r + 1];
-            asm volatile("" : "+v"(x.p[c]), "+v"(ps[bi][i]));
+            asm volatile("" ::"v"(x.p[c]), "v"(ps[bi][i]));
           }
         });
       }
