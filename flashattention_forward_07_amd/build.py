@@ -12,8 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa355.so")
-SOURCES = ["fa355_api.hip", "fa_fwd_kernel.hip", "fa_fwd_pipe.hip", "fa_fwd_f32.hip", "fa_naive.hip",
-           "fa_decode.hip", "fa_small.hip"]
+SOURCES = ["fa355_api.hip", "fa_fwd_kernel.hip", "fa_fwd_pipe.hip", "fa_fwd_ksplit.hip",
+           "fa_fwd_f32.hip", "fa_naive.hip", "fa_decode.hip", "fa_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are switched off for all device code.  Matrix-core

@@ -553,6 +553,15 @@ hipError_t launch_d(const FwdArgs &a, bool causal, bool varlen, hipStream_t stre
 // of 256 gain 27-37 % from the split and of 512 lose 13-15 %; non-causal
 // grids of 256 lose 20 %.
 constexpr long long kSplitMaxGrid = 128;
+// Grid bound of the four-way key split (32-row blocks), from an interleaved
+// A/B against the two-way split above: B1 H8 N1000 d64 causal (256 blocks)
+// 18.6 -> 9.7 us, B2 H4 N1500 d128 causal (376) 34.5 -> 19.3 us, B1 H1
+// N16384 d64 (512) 190 -> 175 us; grids of 1024 and 2048 blocks ran
+// 1.6-1.75x slower with it.
+#ifndef FA_KSPLIT_MAX_GRID
+#define FA_KSPLIT_MAX_GRID 512
+#endif
+constexpr long long kKsplitMaxGrid = FA_KSPLIT_MAX_GRID;
 constexpr long long kSplitMaxGridCausal = 256;
 constexpr int kSplitMinLen = 512;
 
@@ -582,6 +591,16 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
   long long grid = (long long)a.batch * a.H * a.n_qtiles;
   const bool split = a.max_len >= kSplitMinLen &&
                      grid <= (causal ? kSplitMaxGridCausal : kSplitMaxGrid);
+  // Problems that give at most two 32-row query blocks per compute unit run
+  // the four-way key split of fa_fwd_ksplit.hip instead: there the serial key
+  // loop of the heaviest block, not throughput, sets the time.
+  const long long ks_grid =
+      (long long)a.batch * a.H * ((a.max_len + kKsplitBlockM - 1) / kKsplitBlockM);
+  if (ks_grid <= kKsplitMaxGrid) {
+    a.n_qtiles = (a.max_len + kKsplitBlockM - 1) / kKsplitBlockM;
+    a.grid = (int)ks_grid;
+    return launch_fwd_ksplit(a, d, causal, varlen, stream);
+  }
   if (split) {
     a.n_qtiles = (a.max_len + kBlockM / 2 - 1) / (kBlockM / 2);
     grid = (long long)a.batch * a.H * a.n_qtiles;

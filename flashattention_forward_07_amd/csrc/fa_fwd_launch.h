@@ -50,6 +50,12 @@ hipError_t launch_fwd(FwdArgs a, int dtype, int d, bool causal, bool varlen,
 // workgroup, like the 8-wave kernel, so the same grid and tile order.
 hipError_t launch_fwd_pipe(const FwdArgs &a, bool causal, bool varlen, hipStream_t stream);
 
+// The key-split bf16 kernel for small grids (fa_fwd_ksplit.hip): 32 query
+// rows per workgroup, grid = (sequence, head) pairs x n_qtiles.
+hipError_t launch_fwd_ksplit(const FwdArgs &a, int d, bool causal, bool varlen,
+                             hipStream_t stream);
+constexpr int kKsplitBlockM = 32;
+
 // The fp32 kernel (fa_fwd_f32.hip).
 hipError_t launch_fwd_f32(FwdArgs a, int d, bool causal, bool varlen, hipStream_t stream);
 

@@ -299,6 +299,35 @@ def test_varlen_wide_token_rows():
     gu.compare(o, o_ref, lse, lse_ref, "bf16", what="varlen 2 x 512 heads")
 
 
+# --- four-way key split over the waves of a 32-row block (small grids) -------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(1, 16, 1000), (1, 1, 129), (3, 1, 2049), (1, 2, 5000)],
+                         ids=["b1h16n1000", "b1h1n129", "b3h1n2049", "b1h2n5000"])
+def test_ksplit_fixed_full(B, H, N, causal, d):
+    """Problems of at most 512 blocks of 32 query rows: the four waves of a
+    block take every fourth key chunk and merge their partial softmax states
+    at the end.  512 blocks exactly (B1 H16 N1000), a ragged last chunk, a
+    one-row last block (N = 129, past the one-tile path) and 20 chunks per
+    wave (N = 5000); compared in full, outputs NaN-filled beforehand."""
+    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=7700 + N + H + d)
+    o, lse = _run_nan_filled(inp, _scale(d), causal, False)
+    o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, _scale(d), causal)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"ksplit B{B} H{H} N{N} d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_ksplit_wide_scores(d):
+    """Q and K x8 through the four-way split: the running maxima of the four
+    waves differ by hundreds of log2 units when they are merged."""
+    inp = fa_inputs.make_fixed(1, 3, 1500, d, "bf16", seed=7800 + d, qk_mult=8.0)
+    for causal in (False, True):
+        o, lse = _run_nan_filled(inp, _scale(d), causal, False)
+        o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, _scale(d), causal)
+        gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"ksplit x8 d{d} causal={causal}")
+
+
 # --- key range split inside a workgroup (small grids at d = 64) ---------------
 
 @pytest.mark.parametrize("d", [64, 128])
