@@ -13,8 +13,9 @@
 // Workgroup: 4 waves and G = 4 / ceil(N / 32) heads (4 heads of N <= 32,
 // 2 of N <= 64, one otherwise); wave i owns 32 queries of head i / (waves
 // per head).  The workgroup stages the K and V rows of its heads in LDS once
-// (16-byte coalesced loads, zero rows past N), synchronises once, and then
-// every wave works alone:
+// (16-byte coalesced loads, zero rows past N; a compile-time number per
+// thread, all issued before the first LDS write, so that one load latency
+// covers them all), synchronises once, and then every wave works alone:
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (lane l holds query l % 32 and
 //       keys 8 (r / 4) + 4 (l / 32) + r % 4 of each 32-key block in register
 //       r), K rows read from LDS with ds_read_b128 (reading K straight
@@ -95,22 +96,6 @@ __global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_
     if (i < heads_per_wg && h0 + i < n_heads) pair_coords<VARLEN>(a, h0 + i, sn[i], sb[i], lb);
   }
 
-  // ---- stage K and V rows of the workgroup's heads (zeros past each N) ----
-  for (int c = threadIdx.x; c < rows * (D / 8); c += kThreads) {
-    const int row = c / (D / 8), col = 8 * (c % (D / 8));
-    const int slot = row / nb, key = row - slot * nb;
-    const int n_s = slot == 0 ? sn[0] : slot == 1 ? sn[1] : slot == 2 ? sn[2] : sn[3];
-    const long long b_s = slot == 0 ? sb[0] : slot == 1 ? sb[1] : slot == 2 ? sb[2] : sb[3];
-    u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (key < n_s) {  // n_s = 0 for slots past the last head
-      const long long off = b_s + (long long)key * a.row_stride + col;
-      kx = *reinterpret_cast<const u32x4_t *>(kg + off);
-      vx = *reinterpret_cast<const u32x4_t *>(vg + off);
-    }
-    *reinterpret_cast<u32x4_t *>(ks + row * RSK + col) = kx;
-    *reinterpret_cast<u32x4_t *>(vs + row * RSV + col) = vx;
-  }
-
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int l32 = lane & 31, h = lane >> 5;
   const int wph = nb / 32;  // waves per head
@@ -120,17 +105,54 @@ __global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_
   const int qi = 32 * qb + l32;                             // this lane's query
   long long base = 0, lbase = 0;
   int n = 0;  // this wave's sequence length
-  bf16x8_t qr[D / 16];
-  if (active) {
-    pair_coords<VARLEN>(a, bh, n, base, lbase);
+  if (active) pair_coords<VARLEN>(a, bh, n, base, lbase);
+
+  // ---- all loads first: this wave's query rows, then the K and V rows of the
+  // workgroup's heads (a compile-time count per thread, so that every load is
+  // in flight before the first LDS write waits for one) ------------------------
+  u32x4_t qx[D / 16];
+  {
     const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
+    // (unconditional loads from a valid row, zeroed afterwards: no branches
+    // around the loads)
+    const bool qok = active && qi < n;
+    const uint16_t *qp = qg + (qok ? (long long)qi * a.row_stride : 0) + 8 * h;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (qi < n) x = *reinterpret_cast<const u32x4_t *>(qg + (long long)qi * a.row_stride + 16 * c + 8 * h);
-      qr[c] = __builtin_bit_cast(bf16x8_t, x);
+      const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qp + 16 * c);
+      qx[c] = qok ? x : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+  constexpr int PER = kMaxN * (D / 8) / kThreads;  // 16-byte pieces per thread and tensor, at most
+  u32x4_t kx[PER], vx[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    const int row = c / (D / 8), col = 8 * (c % (D / 8));
+    const int sl = row / nb, key = row - sl * nb;
+    const int n_s = sl == 0 ? sn[0] : sl == 1 ? sn[1] : sl == 2 ? sn[2] : sn[3];
+    const long long b_s = sl == 0 ? sb[0] : sl == 1 ? sb[1] : sl == 2 ? sb[2] : sb[3];
+    // n_s = 0 for slots past the last head; zeros past N (the load then reads
+    // the first row of the tensor and is discarded)
+    const bool ok = row < rows && key < n_s;
+    const long long off = ok ? b_s + (long long)key * a.row_stride + col : col;
+    const u32x4_t kk = *reinterpret_cast<const u32x4_t *>(kg + off);
+    const u32x4_t vv = *reinterpret_cast<const u32x4_t *>(vg + off);
+    kx[j] = ok ? kk : u32x4_t{0u, 0u, 0u, 0u};
+    vx[j] = ok ? vv : u32x4_t{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int c = threadIdx.x + j * kThreads;
+    const int row = c / (D / 8), col = 8 * (c % (D / 8));
+    if (row < rows) {
+      *reinterpret_cast<u32x4_t *>(ks + row * RSK + col) = kx[j];
+      *reinterpret_cast<u32x4_t *>(vs + row * RSV + col) = vx[j];
+    }
+  }
+  bf16x8_t qr[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) qr[c] = __builtin_bit_cast(bf16x8_t, qx[c]);
   __syncthreads();
   if (!active) return;
 
