@@ -273,19 +273,52 @@ __global__ __launch_bounds__(kThreads) void small_f32(FwdArgs a, int qblocks) {
   const int t = threadIdx.x, ql = t >> 4, jj = t & 15;
   const int qi = qb * QB + ql;  // this thread's query
 
-  auto stage = [&](const float *src) {  // rows past n are zeros
-    for (int c = t; c < n * (D / 4); c += kThreads) {
+  // The loads go out in rounds of at most 8 per thread: this thread's query
+  // row, then its pieces of the K rows (one round at d = 64, two at d = 128)
+  // and, at d = 64, of the V rows, a compile-time count from valid rows (rows
+  // past n stage duplicates that are never read).  K goes to LDS first; at
+  // d = 64, V waits in registers until the scores are done with K.
+  constexpr int PER = kMaxN * (D / 4) / kThreads;  // 16-byte pieces per thread and tensor
+  constexpr int RND = 8;                            // pieces per round
+  constexpr bool kVEarly = D == 64;
+  static_assert(PER % RND == 0, "rounds");
+  f32x4_t qr[D / 4];
+  {
+    const bool qok = qi < n;
+    const float *qp = qg + (qok ? (long long)qi * a.row_stride : 0);
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t *>(qp + 4 * c);
+      qr[c] = qok ? x : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // pieces per thread that hold rows below n (uniform: the rest are skipped)
+  const int need = (n * (D / 4) + kThreads - 1) / kThreads;
+  auto load = [&](const float *src, f32x4_t *x, int r) {
+#pragma unroll
+    for (int i = 0; i < RND; ++i) {
+      if (r * RND + i >= need) break;
+      const int c = t + (r * RND + i) * kThreads;
       const int row = c / (D / 4), col = 4 * (c % (D / 4));
-      *reinterpret_cast<f32x4_t *>(kv + row * RS + col) =
-          *reinterpret_cast<const f32x4_t *>(src + (long long)row * a.row_stride + col);
+      x[i] = *reinterpret_cast<const f32x4_t *>(src + (long long)(row < n ? row : n - 1) *
+                                                           a.row_stride + col);
     }
   };
-  stage(kg);
-  f32x4_t qr[D / 4];
+  auto store = [&](const f32x4_t *x, int r) {
 #pragma unroll
-  for (int c = 0; c < D / 4; ++c) {
-    qr[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (qi < n) qr[c] = *reinterpret_cast<const f32x4_t *>(qg + (long long)qi * a.row_stride + 4 * c);
+    for (int i = 0; i < RND; ++i) {
+      if (r * RND + i >= need) break;
+      const int c = t + (r * RND + i) * kThreads;
+      const int row = c / (D / 4), col = 4 * (c % (D / 4));
+      *reinterpret_cast<f32x4_t *>(kv + row * RS + col) = x[i];
+    }
+  };
+  f32x4_t px[RND], vx[RND];
+#pragma unroll
+  for (int r = 0; r < PER / RND; ++r) {
+    load(kg, px, r);
+    if (kVEarly && r == 0) load(vg, vx, 0);
+    store(px, r);
   }
   __syncthreads();
 
@@ -325,7 +358,11 @@ __global__ __launch_bounds__(kThreads) void small_f32(FwdArgs a, int qblocks) {
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) l += __shfl_xor(l, off);
   __syncthreads();  // every thread is done with K
-  stage(vg);
+#pragma unroll
+  for (int r = 0; r < PER / RND; ++r) {
+    if (!kVEarly || r > 0) load(vg, vx, r);
+    store(vx, r);
+  }
   __syncthreads();
 
   // 3. O[q][cols] = sum_j p_j V[j][cols]
