@@ -108,7 +108,10 @@ FA_API int fa_fwd(const void *q, const void *k, const void *v, void *o,
  *
  * Preconditions the host cannot check without reading device memory, so
  * the caller guarantees them: cu_seqlens[0] == 0, non-decreasing, and no
- * length above max_seqlen (rows past max_seqlen would be left unwritten).
+ * length above max_seqlen.  A sequence longer than max_seqlen gets
+ * undefined output (rows past max_seqlen are not written, and kernels that
+ * size their key staging by max_seqlen may leave out keys of the rows they
+ * do write); the other sequences are unaffected.
  * o must not overlap q, k, v or lse (only exact pointer equality is
  * detected here, since T is not known on the host).  nseq, H or max_seqlen
  * equal to 0 is an empty problem, as for fa_fwd.  H d above 2^23 elements
