@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_bf16_tile.h"
 #include "fa_common.h"
 #include "fa_small_launch.h"
 
@@ -240,6 +241,307 @@ __global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_
     a.lse[lbase + (long long)qi * a.lse_row_stride] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : neg_inf();
 }
 
+// ---- bf16, N = 97 .. 128, more heads than compute units: staged ahead ------
+// small_bf16 loads a head, computes it and stores it; with two workgroups
+// per compute unit the memory pipe idles whenever both compute, and short
+// heads are bound by that pipe.  Here one workgroup per compute unit (two at
+// d = 64) walks its heads (blockIdx.x, then every gridDim.x-th) and keeps the
+// next heads' loads in flight while it computes:
+//   LDS: a two-head ring of K and V (rows of 64-key blocks, XOR-swizzled as
+//        in the streaming kernels, filled by direct global -> LDS loads) and
+//        one head's query rows, each wave's 32 rows written and read by that
+//        wave alone;
+//   head i: its query rows go to registers and the wave's rows of head
+//        i + 1 to LDS in their place; S, the softmax and P V as in
+//        small_bf16 from ring half i % 2; a barrier; O through the free ring
+//        half to whole-row stores; a barrier; K and V of head i + 2 into ring
+//        half i % 2; a wait for head i + 1's loads; a barrier.
+// Rows past a head's length are loaded as zeros (buffer loads whose range
+// ends with the last row), their scores masked, their outputs not stored.
+// One 16-byte-per-lane global -> LDS load (a plain function: inside a
+// template over the head dimension the builtin leaves the kernel without its
+// host-side stub).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, FA_LDS void *dst,
+                                      uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 1) void small_bf16_stream(FwdArgs a) {
+  using TT = bf16t::Bf16Tile<D, 64>;
+  constexpr int ROWB = TT::ROWB, TILE = TT::TILE, CPR = TT::CPR;
+  constexpr int KV = 2 * TILE;      // 128 rows of K or of V
+  constexpr int BUF = 2 * KV;       // K then V of one head
+  constexpr int QOFF = 2 * BUF;     // one head's query rows
+  constexpr int LDS = QOFF + KV;    // 160 KB at d = 128, 80 KB at d = 64
+  constexpr int M = TILE / 4096;    // loads per wave per 64-row block of K or V
+  constexpr int QL = TILE / 2048;   // loads of a wave's 32 query rows
+  constexpr int NL = 4 * M;         // loads per wave of a head's K and V
+  static_assert(kThreads == 256 && kMaxN == 128, "four waves, 128 rows");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int n_heads = a.batch * a.H;
+  const int G = static_cast<int>(gridDim.x);
+  int head = blockIdx.x;
+  if (head >= n_heads) return;  // uniform, before any barrier
+
+  const long long rs = a.row_stride;
+  const uint32_t rsb = static_cast<uint32_t>(a.row_stride) * 2u;
+  const uint16_t *const qg = static_cast<const uint16_t *>(a.q);
+  const uint16_t *const kg = static_cast<const uint16_t *>(a.k);
+  const uint16_t *const vg = static_cast<const uint16_t *>(a.v);
+  // a head's length and offsets (packed batches read the sequence offsets
+  // with scalar loads, which the staging loads in flight do not hold up)
+  auto coords = [&](int bh, int &n, long long &base, long long &lbase) {
+    const int s = bh / a.H, hd = bh - s * a.H;
+    if constexpr (VARLEN) {
+      using CInt = __attribute__((address_space(4))) const int;
+      CInt *cs = (CInt *)(a.cu_seqlens);
+      const int t0 = cs[s];
+      n = cs[s + 1] - t0;
+      base = (long long)t0 * a.row_stride + (long long)hd * a.head_stride;
+      lbase = (long long)t0 * a.lse_row_stride + (long long)hd * a.lse_head_stride;
+    } else {
+      n = a.n;
+      base = (long long)s * a.seq_stride + (long long)hd * a.head_stride;
+      lbase = (long long)s * a.lse_seq_stride + (long long)hd * a.lse_head_stride;
+    }
+  };
+  auto rows_rec = [&](int valid, int cap) {
+    valid = valid < cap ? valid : cap;
+    return valid > 0 ? (valid - 1) * static_cast<int>(rsb) + ROWB : 0;
+  };
+
+  // ---- staging -------------------------------------------------------------
+  // Load m of wave w in a 64-row block fills the 1 KB of 16-byte slots
+  // p = (w + 4m) * 64 + lane (row p / CPR, slot p % CPR); a wave's query
+  // load j fills slots p = j * 64 + lane of its 32 rows.  Each lane fetches
+  // the logical chunk the swizzle places in its slot.
+  uint32_t o_k[M], o_v[M], o_q[QL];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int p = (w + 4 * m) * kWave + lane, row = p / CPR, slot = p % CPR;
+    o_k[m] = row * rsb + 16u * (slot ^ TT::swz_k(row));
+    o_v[m] = row * rsb + 16u * (slot ^ TT::swz_v(row));
+  }
+#pragma unroll
+  for (int j = 0; j < QL; ++j) {
+    const int p = j * kWave + lane, row = p / CPR, slot = p % CPR;
+    o_q[j] = row * rsb + 16u * (slot ^ TT::swz_k(row));  // (rows 32 w + row: same swizzle)
+  }
+  auto dma_kv = [&](long long base, int n, int buf) {  // n = 0: nothing is read, zeros land
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {  // K rows 0..63, 64..127, then V's
+      const uint16_t *src = (b < 2 ? kg : vg) + base + (long long)(64 * (b & 1)) * rs;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(src), (short)0, rows_rec(n - 64 * (b & 1), 64), 0x00020000);
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        dma16(rsrc, (FA_LDS void *)(smem + buf * BUF + b * TILE + (w + 4 * m) * 1024),
+              b < 2 ? o_k[m] : o_v[m]);
+    }
+  };
+  auto dma_q = [&](long long base, int n) {  // this wave's 32 query rows
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(qg + base + (long long)(32 * w) * rs), (short)0,
+        rows_rec(n - 32 * w, 32), 0x00020000);
+#pragma unroll
+    for (int j = 0; j < QL; ++j)
+      dma16(rsrc, (FA_LDS void *)(smem + QOFF + 32 * w * ROWB + j * 1024), o_q[j]);
+  };
+
+  // ---- LDS operand addresses ------------------------------------------------
+  const uint32_t lds_base =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS char *)smem));
+  uint32_t kofs[D / 16];  // K rows l32 of a 32-key block, chunk 2c + h (also the Q rows)
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    kofs[c] = l32 * ROWB + 16 * ((2 * c + h) ^ TT::swz_k(l32));
+  uint32_t vofs[D / 32];  // V^T operand: rows 4h + e4 (+ 8) of a 16-key step, d 32 db + ..
+  {
+    const int j = lane & 15, e4 = j >> 2, gq = (lane >> 4) & 1;
+    const int sw = TT::swz_v(e4);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      vofs[db] = KV + (4 * h + e4) * ROWB + 16 * ((4 * db + 2 * gq + ((j & 3) >> 1)) ^ sw) +
+                 8 * (j & 1);
+  }
+
+  // ---- prologue: head 0's query rows and K/V, head 1's K/V --------------------
+  int n0, n1 = 0, n2 = 0;
+  long long b0, lb0, b1 = 0, lb1 = 0, b2 = 0, lb2 = 0;
+  coords(head, n0, b0, lb0);
+  bool ok1 = head + G < n_heads;
+  if (ok1) coords(head + G, n1, b1, lb1);
+  dma_q(b0, n0);
+  dma_kv(b0, n0, 0);
+  dma_kv(b1, ok1 ? n1 : 0, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (NL & 15) | ((NL >> 4) << 14));  // all but head 1's K/V
+  bf16t::wg_barrier();
+
+  const int qi = 32 * w + l32;  // this lane's query
+  for (int it = 0;; ++it) {
+    const uint32_t kvb = lds_base + (it & 1) * BUF;
+    // this head's query rows (Q^T operand chunks) into registers, then the
+    // next head's rows to the same LDS
+    bf16x8_t qr[D / 16];
+    {
+      u32x4_t qx[D / 16];
+      const uint32_t qa = lds_base + QOFF + 32 * w * ROWB;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        asm volatile("ds_read_b128 %0, %1" : "=v"(qx[c]) : "v"(qa + kofs[c]));
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(qx[0]));
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        if (c > 0) asm volatile("" : "+v"(qx[c]));
+        qr[c] = __builtin_bit_cast(bf16x8_t, qx[c]);
+      }
+    }
+    dma_q(b1, ok1 ? n1 : 0);
+
+    const int n = n0;
+    const bool active = 32 * w < n;  // wave-uniform
+    f32x16_t o[D / 32];
+    float m = neg_inf(), l = 0.f;
+    if (active) {
+      const int nkb = CAUSAL ? w + 1 : (n + 31) / 32;  // key blocks this wave reads
+      // last visible key of this lane's query, less the lane's key offset
+      // 4h (opaque: otherwise the compiler keeps a lane mask per score
+      // register from before the loop)
+      int lim = n - 1;
+      if constexpr (CAUSAL) lim = lim < qi ? lim : qi;
+      lim -= 4 * h;
+      asm volatile("" : "+v"(lim));
+      // ---- S^T blocks, masked, in log2 units ----
+      f32x16_t sc[kMaxN / 32];
+#pragma unroll
+      for (int kb = 0; kb < kMaxN / 32; ++kb) {
+        if (kb >= nkb) break;  // wave-uniform
+        u32x4_t kx[D / 16];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          asm volatile("ds_read_b128 %0, %1" : "=v"(kx[c]) : "v"(kvb + kofs[c] + 32 * kb * ROWB));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kx[0]));
+        f32x16_t acc = {};
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          if (c > 0) asm volatile("" : "+v"(kx[c]));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx[c]),
+                                                        qr[c], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);  // key - 4h
+          acc[r] = off <= lim ? acc[r] * a.scale_log2 : neg_inf();
+          m = fmaxf(m, acc[r]);
+        }
+        sc[kb] = acc;
+      }
+      m = bf16t::pair_max(m);
+      const float mu = (m == neg_inf()) ? 0.f : m;  // a query with no visible key
+#pragma unroll
+      for (int kb = 0; kb < kMaxN / 32; ++kb) {
+        if (kb >= nkb) break;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[kb][r] = exp2_fast(sc[kb][r] - mu);
+          l += sc[kb][r];
+        }
+      }
+      l = bf16t::pair_sum(l);
+      // ---- O^T = V^T P^T ----
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
+#pragma unroll
+      for (int kb = 0; kb < kMaxN / 32; ++kb) {
+        if (kb >= nkb) break;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {  // 16-key steps: score registers 8 st .. 8 st + 7
+          const uint32_t vb = kvb + (32 * kb + 16 * st) * ROWB;
+          u32x2_t lo[D / 32], hi[D / 32];
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo[db]) : "v"(vb + vofs[db]));
+            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                         : "=v"(hi[db]) : "v"(vb + vofs[db]), "i"(8 * ROWB));
+          }
+          bf16x8_t pb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kb][8 * st + e];
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo[0]), "+v"(hi[0]));
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            if (db > 0) asm volatile("" : "+v"(lo[db]), "+v"(hi[db]));
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16t::cat_bf16(lo[db], hi[db]), pb,
+                                                            o[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+    bf16t::wg_barrier();  // every wave is done with this ring half
+    // ---- O = O^T / l through LDS, lse ----
+    // The wave's 32 output rows go to its quarter of the free ring half's K
+    // rows (row-major, 16-byte chunk c of row r in slot c ^ (r % CPR)), then
+    // back as whole 16-byte chunks, so that the stores cover whole rows
+    // (the score layout would give every store 32 row pieces of 16 bytes).
+    if (active) {
+      const uint32_t ob = kvb + 32 * w * ROWB;
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const bf16x4_t x = {(__bf16)(o[db][4 * gq] * inv), (__bf16)(o[db][4 * gq + 1] * inv),
+                              (__bf16)(o[db][4 * gq + 2] * inv), (__bf16)(o[db][4 * gq + 3] * inv)};
+          const uint32_t ad = ob + l32 * ROWB + 16 * ((4 * db + gq) ^ (l32 % CPR)) + 8 * h;
+          asm volatile("ds_write_b64 %0, %1" ::"v"(ad), "v"(__builtin_bit_cast(u32x2_t, x))
+                       : "memory");
+        }
+      if (h == 0 && a.lse != nullptr && qi < n)
+        a.lse[lb0 + (long long)qi * a.lse_row_stride] =
+            (l > 0.f) ? (m + __log2f(l)) * kLn2 : neg_inf();
+      uint16_t *const og = static_cast<uint16_t *>(a.o) + b0;
+      constexpr int OL = 32 * CPR / kWave;  // 16-byte chunks per lane
+      u32x4_t y[OL];
+#pragma unroll
+      for (int j = 0; j < OL; ++j) {
+        const int p = j * kWave + lane, r = p / CPR, c = p % CPR;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(y[j]) : "v"(ob + r * ROWB + 16 * (c ^ (r % CPR))));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(y[0]));
+#pragma unroll
+      for (int j = 0; j < OL; ++j) {
+        if (j > 0) asm volatile("" : "+v"(y[j]));
+        const int p = j * kWave + lane, r = p / CPR, c = p % CPR;
+        if (32 * w + r < n)
+          *reinterpret_cast<u32x4_t *>(og + (long long)(32 * w + r) * rs + 8 * c) = y[j];
+      }
+    }
+    bf16t::wg_barrier();  // every wave has read its rows back
+
+    // K and V of the head after next into the ring half just freed, then wait
+    // for the next head's loads (the wait also covers this head's stores,
+    // issued before them)
+    const bool ok2 = ok1 && head + 2 * G < n_heads;
+    if (ok2) coords(head + 2 * G, n2, b2, lb2);
+    dma_kv(b2, ok2 ? n2 : 0, it & 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL & 15) | ((NL >> 4) << 14));
+    bf16t::wg_barrier();
+    if (!ok1) break;
+    head += G;
+    n0 = n1; b0 = b1; lb0 = lb1;
+    n1 = n2; b1 = b2; lb1 = lb2;
+    ok1 = ok2;
+  }
+  // no staging load outlives the workgroup (the last ones, past the last
+  // head, move no memory)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // ---- fp32 ------------------------------------------------------------------
 // fp32 has no fast matrix path worth its set-up at this size (the fp32
 // matrix cores and the vector ALU have the same peak), so this variant
@@ -405,11 +707,37 @@ hipError_t run_f32(const FwdArgs &a, bool causal, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
 template <int D, bool VARLEN>
 hipError_t run(const FwdArgs &a, bool causal, hipStream_t st) {
   const int nb = (a.max_len + 31) & ~31;
   const int heads_per_wg = 4 / (nb / 32);  // 4, 2, 1, 1
   const long long n_heads = (long long)a.batch * a.H;
+  // Heads of 97 .. 128 rows, more of them than the workgroups a GPU holds at
+  // once: the staged-ahead variant, one workgroup per compute unit (two at
+  // d = 64) working through its heads.
+  const long long resident = (long long)device_cus() * (D == 64 ? 2 : 1);
+  if (nb == kMaxN && resident > 0 && n_heads > resident) {
+    if (causal)
+      hipLaunchKernelGGL((small_bf16_stream<D, true, VARLEN>), dim3((unsigned)resident),
+                         dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((small_bf16_stream<D, false, VARLEN>), dim3((unsigned)resident),
+                         dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+  }
   const long long grid = (n_heads + heads_per_wg - 1) / heads_per_wg;
   if (grid <= 0 || grid > 0x7fffffffll) return hipErrorInvalidValue;
   if (causal)

@@ -83,3 +83,43 @@ def test_one_tile_and_general_kernel_meet_at_128():
     o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, scale, True)
     gu.compare(o129, o_ref, l129, lse_ref, "bf16", what="N=129")
     gu.compare(o128, o_ref[:, :, :128], l128, lse_ref[:, :, :128], "bf16", what="N=128")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [97, 100, 128])
+def test_one_tile_staged_ahead_full(d, causal, N):
+    """Heads of 97..128 rows, more of them than the GPU holds workgroups at
+    once (605 > 2 per compute unit at d = 64, 1 at d = 128): the one-tile
+    kernel that stages the next heads while it computes. Every head is
+    compared in full; the outputs start as NaN."""
+    B, H = 5, 121
+    print(f"case one-tile staged d={d} causal={causal} B={B} H={H} N={N}", flush=True)
+    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=5300 + N + d + int(causal))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = _run(inp, scale, causal)
+    o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, scale, causal)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what=f"staged N={N}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_tile_staged_ahead_varlen_full(d, causal):
+    """A packed batch of 700 sequences x 2 heads, lengths 0..128 with the
+    longest 128 (so the staged one-tile kernel runs), every row compared."""
+    rng = np.random.default_rng(5400 + d + int(causal))
+    lengths = [int(x) for x in rng.integers(0, 129, size=700)]
+    lengths[0], lengths[1], lengths[2] = 128, 0, 1
+    print(f"case one-tile staged varlen d={d} causal={causal}", flush=True)
+    inp = fa_inputs.make_varlen(lengths, 2, d, "bf16", rng)
+    q, k, v = gu.upload(inp)
+    T = q.shape[0]
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((T, 2), float("nan"), dtype=torch.float32, device="cuda")
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    cu = torch.from_numpy(inp.cu_seqlens).cuda()
+    fa.fa_fwd_varlen(q, k, v, o, lse, cu, len(lengths), max(lengths), 2, d, scale, causal,
+                     fa.FA_DTYPE_BF16)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, scale, causal)
+    gu.compare(o, o_ref, lse, lse_ref, "bf16", what="staged varlen")
