@@ -155,90 +155,110 @@ __global__ __launch_bounds__(kThreads) void small_bf16(FwdArgs a, int heads_per_
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) qr[c] = __builtin_bit_cast(bf16x8_t, qx[c]);
   __syncthreads();
-  if (!active) return;
 
-  // key blocks this wave needs: all of the head's, or (causal) up to its own
-  const int nkb = CAUSAL ? qb + 1 : wph;
   const int krow0 = slot * nb;  // first LDS row of this head
-
-  // ---- S^T blocks, masked, in log2 units ----
-  f32x16_t sc[kMaxN / 32];
-  float m = neg_inf();
-#pragma unroll
-  for (int kb = 0; kb < kMaxN / 32; ++kb) {
-    if (kb >= nkb) break;  // wave-uniform
-    f32x16_t acc = {};
-    const uint16_t *krow = ks + (krow0 + 32 * kb + l32) * RSK + 8 * h;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(krow + 16 * c);  // ds_read_b128
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qr[c], acc,
-                                                    0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * kb + block_key(r, h);
-      const bool vis = key < n && (!CAUSAL || key <= qi);
-      acc[r] = vis ? acc[r] * a.scale_log2 : neg_inf();
-      m = fmaxf(m, acc[r]);
-    }
-    sc[kb] = acc;
-  }
-  m = fmaxf(m, __shfl_xor(m, 32));
-  const float mu = (m == neg_inf()) ? 0.f : m;  // a query with no visible key
-  float l = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < kMaxN / 32; ++kb) {
-    if (kb >= nkb) break;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[kb][r] = exp2_fast(sc[kb][r] - mu);
-      l += sc[kb][r];
-    }
-  }
-  l += __shfl_xor(l, 32);
-
-  // ---- O^T = V^T P^T ----
   f32x16_t o[D / 32];
+  float m = neg_inf(), l = 0.f;
+  if (active) {
+    // key blocks this wave needs: all of the head's, or (causal) up to its own
+    const int nkb = CAUSAL ? qb + 1 : wph;
+
+    // ---- S^T blocks, masked, in log2 units ----
+    f32x16_t sc[kMaxN / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-  const int g = lane >> 4, j = lane & 15;
-  // first transposing read: rows 4 (g / 2) + j / 4 of the 16-key step,
-  // columns 16 (g % 2) + 4 (j % 4); the second read is 8 rows further
-  const uint16_t *va = vs + (krow0 + 4 * (g >> 1) + (j >> 2)) * RSV + 16 * (g & 1) + 4 * (j & 3);
+    for (int kb = 0; kb < kMaxN / 32; ++kb) {
+      if (kb >= nkb) break;  // wave-uniform
+      f32x16_t acc = {};
+      const uint16_t *krow = ks + (krow0 + 32 * kb + l32) * RSK + 8 * h;
 #pragma unroll
-  for (int kb = 0; kb < kMaxN / 32; ++kb) {
-    if (kb >= nkb) break;
+      for (int c = 0; c < D / 16; ++c) {
+        const u32x4_t kx = *reinterpret_cast<const u32x4_t *>(krow + 16 * c);  // ds_read_b128
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx), qr[c], acc,
+                                                      0, 0, 0);
+      }
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {  // 16-key steps: score registers 8 st .. 8 st + 7
-      bf16x8_t pb;
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + block_key(r, h);
+        const bool vis = key < n && (!CAUSAL || key <= qi);
+        acc[r] = vis ? acc[r] * a.scale_log2 : neg_inf();
+        m = fmaxf(m, acc[r]);
+      }
+      sc[kb] = acc;
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float mu = (m == neg_inf()) ? 0.f : m;  // a query with no visible key
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kb][8 * st + e];
+    for (int kb = 0; kb < kMaxN / 32; ++kb) {
+      if (kb >= nkb) break;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t *ad = va + (32 * kb + 16 * st) * RSV + 32 * db;
-        const u32x2_t lo = tr_read(ad), hi = tr_read(ad + 8 * RSV);
-        const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[db],
-                                                        0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        sc[kb][r] = exp2_fast(sc[kb][r] - mu);
+        l += sc[kb][r];
+      }
+    }
+    l += __shfl_xor(l, 32);
+
+    // ---- O^T = V^T P^T ----
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
+    const int g = lane >> 4, j = lane & 15;
+    // first transposing read: rows 4 (g / 2) + j / 4 of the 16-key step,
+    // columns 16 (g % 2) + 4 (j % 4); the second read is 8 rows further
+    const uint16_t *va = vs + (krow0 + 4 * (g >> 1) + (j >> 2)) * RSV + 16 * (g & 1) + 4 * (j & 3);
+#pragma unroll
+    for (int kb = 0; kb < kMaxN / 32; ++kb) {
+      if (kb >= nkb) break;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {  // 16-key steps: score registers 8 st .. 8 st + 7
+        bf16x8_t pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sc[kb][8 * st + e];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const uint16_t *ad = va + (32 * kb + 16 * st) * RSV + 32 * db;
+          const u32x2_t lo = tr_read(ad), hi = tr_read(ad + 8 * RSV);
+          const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[db],
+                                                          0, 0, 0);
+        }
       }
     }
   }
 
-  // ---- O = O^T / l, lse ----
-  if (qi >= n) return;
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  uint16_t *orow = static_cast<uint16_t *>(a.o) + base + (long long)qi * a.row_stride;
+  // ---- O = O^T / l through LDS, lse ----
+  // Once every wave is done with K and V, each wave stages its 32 output
+  // rows in its own 32 staged K rows and reads them back as whole 16-byte
+  // row chunks, so that the stores cover whole rows (the score layout would
+  // give every store 32 row pieces of 16 bytes).
+  __syncthreads();
+  if (!active) return;
+  {
+    uint16_t *const st = ks + (krow0 + 32 * qb) * RSK;
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const bf16x4_t x = {(__bf16)(o[db][4 * gq] * inv), (__bf16)(o[db][4 * gq + 1] * inv),
-                          (__bf16)(o[db][4 * gq + 2] * inv), (__bf16)(o[db][4 * gq + 3] * inv)};
-      *reinterpret_cast<bf16x4_t *>(orow + 32 * db + 8 * gq + 4 * h) = x;
-    }
-  if (h == 0 && a.lse != nullptr)
+      for (int gq = 0; gq < 4; ++gq) {
+        const bf16x4_t x = {(__bf16)(o[db][4 * gq] * inv), (__bf16)(o[db][4 * gq + 1] * inv),
+                            (__bf16)(o[db][4 * gq + 2] * inv), (__bf16)(o[db][4 * gq + 3] * inv)};
+        *reinterpret_cast<bf16x4_t *>(st + l32 * RSK + 32 * db + 8 * gq + 4 * h) = x;
+      }
+  }
+  if (h == 0 && a.lse != nullptr && qi < n)
     a.lse[lbase + (long long)qi * a.lse_row_stride] = (l > 0.f) ? (m + __log2f(l)) * kLn2 : neg_inf();
+  {
+    constexpr int CH = D / 8;                // 16-byte chunks per row
+    constexpr int OL = 32 * CH / kWave;      // per lane
+    const uint16_t *const st = ks + (krow0 + 32 * qb) * RSK;
+    uint16_t *const og = static_cast<uint16_t *>(a.o) + base;
+#pragma unroll
+    for (int j = 0; j < OL; ++j) {
+      const int p = j * kWave + lane, r = p / CH, c = p % CH;
+      const u32x4_t y = *reinterpret_cast<const u32x4_t *>(st + r * RSK + 8 * c);
+      if (32 * qb + r < n)
+        *reinterpret_cast<u32x4_t *>(og + (long long)(32 * qb + r) * a.row_stride + 8 * c) = y;
+    }
+  }
 }
 
 // ---- bf16, N = 97 .. 128, more heads than compute units: staged ahead ------
