@@ -352,16 +352,35 @@ def _timed(torch, fn, reps, warmup):
     return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
+def _timed_back_to_back(torch, fn, reps, warmup):
+    """Mean launch time of reps launches issued back to back between two
+    events (as the workload bench times its steps)."""
+    for _ in range(warmup):
+        fn()
+    st = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(st)
+    for _ in range(reps):
+        fn()
+    b.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def compare_short(torch, fa, reps=50, warmup=10):
     """Many short sequences (one head each, causal, bf16 and fp32): fa_fwd,
     which takes the one-tile kernels for N <= 128 (fp32 only while
     latency-bound), against the general streaming kernel on the same data
     (fa_fwd_varlen with equal lengths and max_seqlen 129: with one head the
     packed and the fixed layouts coincide) and the naive method.  Median
-    launch times."""
+    launch times, each launch between its own pair of events; for fa_fwd also
+    the mean over launches issued back to back (where one launch's last
+    workgroups overlap the next one's first), and the compulsory bytes per
+    second of both."""
     print("| dtype | d | sequences | N | fa_fwd path | fa_fwd us | general kernel us | naive us | "
-          "fa_fwd GB/s | general / fa_fwd |")
-    print("|---|---|---:|---:|---|---:|---:|---:|---:|---:|")
+          "fa_fwd GB/s | general / fa_fwd | fa_fwd us, back to back | GB/s, back to back |")
+    print("|---|---|---:|---:|---|---:|---:|---:|---:|---:|---:|---:|")
     for dtype, d, B, N in [(dt, d, B, N) for dt in ("bf16", "f32") for d in (64, 128)
                            for B in (1, 1024, 8192) for N in (16, 64, 128)]:
                 inp = fa_inputs.make_fixed(B, 1, N, d, dtype, seed=9500 + N + d)
@@ -388,15 +407,19 @@ def compare_short(torch, fa, reps=50, warmup=10):
                                                             scale, True, code), reps, warmup)
                 t3 = _timed(torch, lambda: fa.fa_naive_fwd(q, k, v, o3, l3, ws, wsb, B, 1, N, d,
                                                            scale, True, code), reps, warmup)
+                t4 = _timed_back_to_back(torch, lambda: fa.fa_fwd(q, k, v, o1, l1, B, 1, N, d, scale,
+                                                                  True, code), reps, warmup)
                 diff = (o1.float() - o2.float()).abs().max().item()
                 if diff > (2e-2 if dtype == "bf16" else 2e-5):
                     raise SystemExit(f"one-tile and general kernel disagree by {diff}")
                 gbs = algorithmic_bytes(B * N, 1, d, elem) / (t1 * 1e-3) / 1e9
+                gbs4 = algorithmic_bytes(B * N, 1, d, elem) / (t4 * 1e-3) / 1e9
                 # the library's rule: bf16 always one-tile; fp32 while latency-bound
                 path = ("one-tile" if dtype == "bf16" or N <= 32 or 4.0 * B * N * N * d <= 2 ** 28
                         else "general")
                 print(f"| {dtype} | {d} | {B} | {N} | {path} | {t1 * 1e3:.1f} | {t2 * 1e3:.1f} | "
-                      f"{t3 * 1e3:.1f} | {gbs:.0f} | {t2 / t1:.2f} |", flush=True)
+                      f"{t3 * 1e3:.1f} | {gbs:.0f} | {t2 / t1:.2f} | {t4 * 1e3:.1f} | {gbs4:.0f} |",
+                      flush=True)
 
 
 def compare_naive(torch, fa, reps=20, warmup=5):
