@@ -567,11 +567,15 @@ constexpr int kSplitMinLen = 512;
 
 // Heads of one XCD scheduled together (tile_order): the largest divisor of
 // its head count up to kGroupHeads, so that the 32 CUs of an XCD run about
-// four workgroups on each head's K/V stream at once.  Measured on the packed
-// 16-sequence causal workload (64 heads per XCD): 729 TFLOP/s with all heads
-// in one group, 878 with groups of 8, 882 with 4, 818 with 1; fixed-length
-// workloads within +-1 % of one group.
-constexpr int kGroupHeads = 8;
+// eight workgroups on each head's K/V stream at once.  Interleaved A/B of
+// the group size on B4 H32 N4096 d128 causal (16 heads per XCD), with the
+// K/V bytes fetched from beyond L2 (FETCH_SIZE, per launch, against the
+// compulsory Q + K + V):
+//   group 1: 617 us, 1.00x;  2: 545 us, 1.32x;  4: 545 us, 1.38x;
+//   8: 560 us, 2.15x;        16: 569 us, 3.59x.
+// On the packed 16-sequence causal workload (64 heads per XCD) groups of 4
+// and 8 tie (3560 and 3568 us), 2 is 3 % slower and 1 is 8 % slower.
+constexpr int kGroupHeads = 4;
 int head_group(int n_heads) {
   if (n_heads % kXcds != 0) return 0;
   const int hx = n_heads / kXcds;
