@@ -16,9 +16,9 @@ namespace bf16t {
 template <int D, int BN_>
 struct Bf16Tile {
   static constexpr int BN = BN_;
-  // (32 keys: the key-split mode at d = 128, whose two rings of 64-key tiles
-  // would not fit in LDS)
-  static_assert(BN == 64 || (BN == 128 && D == 64) || (BN == 32 && D == 128), "keys per tile");
+  // (32 keys: the key-split kernel, whose per-wave rings would not fit in
+  // LDS with 64-key tiles)
+  static_assert(BN == 64 || (BN == 128 && D == 64) || BN == 32, "keys per tile");
   static constexpr int ROWB = D * 2;              // bytes per K/V row
   static constexpr int TILE = BN * ROWB;          // bytes per K (or V) tile
   static constexpr int STAGE = 2 * TILE;          // K tile then V tile

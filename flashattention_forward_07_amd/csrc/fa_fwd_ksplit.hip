@@ -4,14 +4,15 @@
 //
 // There the time of a launch is the serial key loop of its heaviest query
 // tile, not throughput.  So each workgroup takes only 32 query rows, and
-// its four waves (one per SIMD) split the key range of those rows among
-// them: wave w streams key chunks w, w + 4, w + 8, ... through a two-stage
-// LDS ring of its own, keeps a partial softmax state for all 32 rows, and
-// needs no barrier until the end.  Then the four partial states are merged
+// its W waves (eight at d = 64, two per SIMD; four at d = 128) split the
+// key range of those rows among them: wave w streams 32-key chunks w,
+// w + W, w + 2W, ... through a two-stage LDS ring of its own, keeps a
+// partial softmax state for all 32 rows, and needs no barrier until the
+// end.  Then the W partial states are merged
 // through LDS, each term weighted by 2^(its reference - the largest), which
 // is the exact combination of partial softmax sums, and O / l is written.
 //
-// Per chunk (64 keys at d = 64, 32 at d = 128), one wave runs the steps of
+// Per chunk, one wave runs the steps of
 // the resident-query loop of "Mini FlashAttention", section 4: S^T = K Q^T on
 // v_mfma_f32_32x32x16_bf16 (one query per lane, 16 keys of each 32-key block
 // per lane half), the causal and sequence-end mask (section 1), the chunk's
@@ -40,22 +41,23 @@ namespace {
 
 using namespace bf16t;
 
-constexpr int kKsWaves = 4;
-constexpr int kKsThreads = kWave * kKsWaves;  // 256
 constexpr int kKsRows = 32;                   // query rows per workgroup
 
 template <int D>
 struct KsShape {
-  static constexpr int BN = D == 64 ? 64 : 32;  // keys per chunk
+  static constexpr int W = D == 64 ? 8 : 4;       // waves: two per SIMD at d = 64
+  static constexpr int THREADS = W * kWave;
+  static constexpr int BN = 32;                   // keys per chunk
   using Tile = Bf16Tile<D, BN>;
-  static constexpr int RING = 2 * Tile::STAGE;  // two stages per wave: 32 KB
+  static constexpr int RING = 2 * Tile::STAGE;    // two stages per wave: 16 or 32 KB
   static constexpr int DPW = Tile::TILE / 1024;  // staging loads per tensor and chunk
   static constexpr int NW = (D / 32) * 16 + 3;   // floats per lane of a partial state
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kKsThreads) void fa_fwd_ksplit(const FwdArgs a) {
+__global__ __launch_bounds__(KsShape<D>::THREADS) void fa_fwd_ksplit(const FwdArgs a) {
   using S = KsShape<D>;
+  constexpr int kKsWaves = S::W;
   using C = typename S::Tile;
   constexpr int BN = S::BN;
   constexpr int KB = BN / 32;       // 32-key blocks per chunk
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(kKsThreads) void fa_fwd_ksplit(const FwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: no staging load outlives the loop
 
-  // ---- merge the four partial states through LDS -----------------------------
+  // ---- merge the W partial states through LDS --------------------------------
   wg_barrier();  // every wave is done with its ring
   float *part = reinterpret_cast<float *>(smem);
   {
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(kKsThreads) void fa_fwd_ksplit(const FwdArgs a) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_ks(const FwdArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_ksplit<D, CAUSAL, VARLEN>), dim3(a.grid), dim3(kKsThreads), 0,
+  hipLaunchKernelGGL((fa_fwd_ksplit<D, CAUSAL, VARLEN>), dim3(a.grid), dim3(KsShape<D>::THREADS), 0,
                      stream, a);
   return hipGetLastError();
 }
