@@ -51,7 +51,7 @@ struct KsShape {
   using Tile = Bf16Tile<D, BN>;
   static constexpr int RING = 2 * Tile::STAGE;    // two stages per wave: 16 or 32 KB
   static constexpr int DPW = Tile::TILE / 1024;  // staging loads per tensor and chunk
-  static constexpr int NW = (D / 32) * 16 + 3;   // floats per lane of a partial state
+  static constexpr int NV = (D / 32) * 4 + 1;       // float4 slots per lane of a partial state
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(KsShape<D>::THREADS) void fa_fwd_ksplit(const FwdAr
   // s_waitcnt immediate for vmcnt(2 DPW) (low four bits, then bits 14-15),
   // lgkmcnt and expcnt at their maxima
   constexpr int kVmcntNext = ((2 * DPW) & 15) | (((2 * DPW) >> 4) << 14) | 0x0F70;
-  static_assert(kKsWaves * S::NW * kWave * 4 <= kKsWaves * S::RING, "merge area");
+  static_assert(kKsWaves * S::NV * kWave * 16 <= kKsWaves * S::RING, "merge area");
   __shared__ __attribute__((aligned(1024))) char smem[kKsWaves * S::RING];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -280,36 +280,46 @@ __global__ __launch_bounds__(KsShape<D>::THREADS) void fa_fwd_ksplit(const FwdAr
 
   // ---- merge the W partial states through LDS --------------------------------
   wg_barrier();  // every wave is done with its ring
-  float *part = reinterpret_cast<float *>(smem);
+  // per wave and lane: O in float4 slots (d block db, quarter j at slot
+  // 4 db + j) and (max, l, rounded-weight sum) in the last slot; slot s of
+  // wave v at f32x4 index (v NV + s) 64 + lane, so that every access is one
+  // 16-byte read or write per lane over consecutive lanes
+  f32x4_t *part = reinterpret_cast<f32x4_t *>(smem);
+  constexpr int NV = S::NV;
   {
-    float *mine = part + (w * S::NW) * kWave + lane;
+    f32x4_t *mine = part + (w * NV) * kWave + lane;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mine[(db * 16 + r) * kWave] = o[db][r];
-    mine[(S::NW - 3) * kWave] = mref;
-    mine[(S::NW - 2) * kWave] = l_run;
-    mine[(S::NW - 1) * kWave] = lr_run;
+      for (int j = 0; j < 4; ++j)
+        mine[(db * 4 + j) * kWave] =
+            f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
+    mine[(NV - 1) * kWave] = f32x4_t{mref, l_run, lr_run, 0.f};
   }
   wg_barrier();
   // wave w finishes d block w (d = 64: waves 0 and 1); wave 0 also writes lse
   if (w >= D / 32) return;
-  float mv[kKsWaves], mm = neg_inf();
+  f32x4_t sv[kKsWaves];
+  float mm = neg_inf();
 #pragma unroll
   for (int v = 0; v < kKsWaves; ++v) {
-    mv[v] = part[(v * S::NW + S::NW - 3) * kWave + lane];
-    mm = __builtin_fmaxf(mm, mv[v]);
+    sv[v] = part[(v * NV + NV - 1) * kWave + lane];
+    mm = __builtin_fmaxf(mm, sv[v][0]);
   }
   f32x16_t acc = f32x16_t{};
   float l_tot = 0.f, lr_tot = 0.f;
 #pragma unroll
   for (int v = 0; v < kKsWaves; ++v) {
-    const float f = mv[v] == neg_inf() ? 0.f : exp2_fast(mv[v] - mm);
-    const float *pv = part + (v * S::NW) * kWave + lane;
+    const float f = sv[v][0] == neg_inf() ? 0.f : exp2_fast(sv[v][0] - mm);
+    const f32x4_t *pv = part + (v * NV + 4 * w) * kWave + lane;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += f * pv[(w * 16 + r) * kWave];
-    l_tot += f * pv[(S::NW - 2) * kWave];
-    lr_tot += f * pv[(S::NW - 1) * kWave];
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t x = pv[j * kWave];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * j + e] += f * x[e];
+    }
+    l_tot += f * sv[v][1];
+    lr_tot += f * sv[v][2];
   }
   l_tot = pair_sum(l_tot);
   lr_tot = pair_sum(lr_tot);
