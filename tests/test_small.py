@@ -123,3 +123,17 @@ def test_one_tile_staged_ahead_varlen_full(d, causal):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_varlen(inp.q, inp.k, inp.v, inp.cu_seqlens, scale, causal)
     gu.compare(o, o_ref, lse, lse_ref, "bf16", what="staged varlen")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_tile_staged_ahead_without_lse(d):
+    """The staged one-tile kernel with lse = NULL: O still matches in full."""
+    B, H, N = 3, 200, 120
+    inp = fa_inputs.make_fixed(B, H, N, d, "bf16", seed=5500 + d)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    q, k, v = gu.upload(inp)
+    o = torch.full_like(q, float("nan"))
+    fa.fa_fwd(q, k, v, o, None, B, H, N, d, scale, True, fa.FA_DTYPE_BF16)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(inp.q, inp.k, inp.v, scale, True)
+    gu.compare(o, o_ref, None, None, "bf16", what="staged, no lse")
