@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa_bf16_tile.h"
 #include "fa_common.h"
 #include "fa_small_launch.h"
@@ -727,16 +729,20 @@ hipError_t run_f32(const FwdArgs &a, bool causal, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (cached per device; 0 if unknown).
+// Compute units of the current device (cached per device; 0 if unknown,
+// which keeps the plain one-tile kernel).
 int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (dev < 64) cached[dev] = cus;
+  if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
