@@ -59,7 +59,9 @@
 // chunks, filled by direct global->LDS buffer loads (each wave moves a quarter
 // of a tile).  After the barrier that opens iteration t, the K tile t+1 and
 // the V tiles up to t have landed and tile t-2's stage is free; the loads of
-// tile t+2 go out early in the body, K before V.
+// tile t+2 go out early in the body, K before V.  The workgroup's query rows
+// come in the same way, through stages 2 and 3 before the ring first uses
+// them, and are read from there into the Q^T AGPRs.
 //
 // Masking: keys past the sequence end and (causal) keys after the query score
 // -inf ("Mini FlashAttention", section 1); a -inf reference is replaced by 0
@@ -236,17 +238,32 @@ __device__ __forceinline__ void lds_read_k(u32x4_t &d, uint32_t addr) {
   FA_RK(3, "a[252:255]")
 #undef FA_RK
 }
+// Q^T chunks of a block from LDS (laid out as a K tile) into their AGPRs;
+// q_settle awaits them.
+template <int BLK, class QB>
+__device__ __forceinline__ void q_read(QB &x, uint32_t base, const uint32_t *ofs) {
+#define FA_RQ(C_, ALL)                                                                  \
+  asm volatile("ds_read_b128 %0, %1" : "={" ALL "}"(x.q[C_]) : "v"(base + ofs[C_]));
+  if constexpr (BLK == 0) {
+    FA_RQ(0, "a[128:131]") FA_RQ(1, "a[132:135]") FA_RQ(2, "a[136:139]") FA_RQ(3, "a[140:143]")
+    FA_RQ(4, "a[144:147]") FA_RQ(5, "a[148:151]") FA_RQ(6, "a[152:155]") FA_RQ(7, "a[156:159]")
+  } else {
+    FA_RQ(0, "a[160:163]") FA_RQ(1, "a[164:167]") FA_RQ(2, "a[168:171]") FA_RQ(3, "a[172:175]")
+    FA_RQ(4, "a[176:179]") FA_RQ(5, "a[180:183]") FA_RQ(6, "a[184:187]") FA_RQ(7, "a[188:191]")
+  }
+#undef FA_RQ
+}
 template <int BLK, class QB>
 __device__ __forceinline__ void q_settle(QB &x) {
   // after the Q^T chunks are written to their AGPRs: wait states before a
   // product reads them
   if constexpr (BLK == 0)
-    asm volatile("s_nop 4"
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 4"
                  : "+{a[128:131]}"(x.q[0]), "+{a[132:135]}"(x.q[1]), "+{a[136:139]}"(x.q[2]),
                    "+{a[140:143]}"(x.q[3]), "+{a[144:147]}"(x.q[4]), "+{a[148:151]}"(x.q[5]),
                    "+{a[152:155]}"(x.q[6]), "+{a[156:159]}"(x.q[7]));
   else
-    asm volatile("s_nop 4"
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 4"
                  : "+{a[160:163]}"(x.q[0]), "+{a[164:167]}"(x.q[1]), "+{a[168:171]}"(x.q[2]),
                    "+{a[172:175]}"(x.q[3]), "+{a[176:179]}"(x.q[4]), "+{a[180:183]}"(x.q[5]),
                    "+{a[184:187]}"(x.q[6]), "+{a[188:191]}"(x.q[7]));
@@ -482,20 +499,6 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   QBlock<1> B;
   A.q0 = q0;
   B.q0 = q0 + 32;
-  {
-#pragma unroll
-    for (int c = 0; c < kPD / 16; ++c) {
-      // rows past the end load row n - 1 and are zeroed (they are never stored)
-      const int ra = A.q0 + l32, rb = B.q0 + l32;
-      u32x4_t xa = *reinterpret_cast<const u32x4_t *>(qg + (long long)(ra < n ? ra : n - 1) * rs +
-                                                      8 * h + 16 * c);
-      u32x4_t xb = *reinterpret_cast<const u32x4_t *>(qg + (long long)(rb < n ? rb : n - 1) * rs +
-                                                      8 * h + 16 * c);
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      A.q[c] = __builtin_bit_cast(bf16x8_t, ra < n ? xa : z);
-      B.q[c] = __builtin_bit_cast(bf16x8_t, rb < n ? xb : z);
-    }
-  }
 #pragma unroll
   for (int db = 0; db < kPD / 32; ++db) {
     A.o[db] = f32x16_t{};
@@ -505,8 +508,6 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   B.lr = f32x4_t{};
   acc_settle(A);  // places the zeroed accumulators in AGPRs
   acc_settle(B);
-  q_settle<0>(A);  // ... and Q^T in its AGPRs
-  q_settle<1>(B);
   {
     const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -829,11 +830,36 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   using T_ = std::true_type;
   using F_ = std::false_type;
 
-  // prologue: tiles 0 and 1 requested, tile 0's K in LDS, S(0)
+  // prologue: the query rows staged through stages 2 and 3 (piece j, rows
+  // m0 + 64 j .. + 63, laid out as a K tile; wave w moves a quarter of each
+  // piece with the K tile's offsets), tiles 0 and 1 requested; once the query
+  // rows and tile 0's K are in LDS, Q^T goes to its AGPRs and S(0) runs
+#pragma unroll
+  for (int j = 0; j < kPBlockM / kPBN; ++j) {
+    const int r0 = m0 + j * kPBN;
+    const int valid = n - r0 < kPBN ? (n - r0 > 0 ? n - r0 : 0) : kPBN;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(qg + (long long)r0 * rs), (short)0,
+        __builtin_amdgcn_readfirstlane(valid > 0 ? (int)((valid - 1) * rsb + PT::ROWB) : 0),
+        0x00020000);
+#pragma unroll
+    for (int i = 0; i < kPDpw; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (FA_LDS void *)(smem + 2 * PT::STAGE + j * PT::TILE + (w * kPDpw + i) * 1024), 16,
+          o_k[i], 0, 0, 0);
+  }
   dma_tile(0);
   dma_tile(1);
-  __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt 12: tile 0's K landed
+  __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt 12: the query rows and tile 0's K landed
   wg_barrier();
+  {
+    // wave w's rows are piece w: block a its rows 0 .. 31, block b 32 .. 63
+    const uint32_t qa = lds_base + 2 * PT::STAGE + w * PT::TILE;
+    q_read<0>(A, qa, kofs);
+    q_read<1>(B, qa + 32 * PT::ROWB, kofs);
+  }
+  q_settle<0>(A);  // (awaits the reads)
+  q_settle<1>(B);
   if (Tw > 0) {
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -867,7 +893,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
 
   // ---- finalise: O / (rounded-weight sum), lse = ln 2 (m + log2 l) ----------
   // The lane index again, opaque to the compiler, so that the output
-  // addresses are computed here rather than kept from the query loads through
+  // addresses are computed here rather than kept from the prologue through
   // the loop, where they would take registers the loop needs.
   int lane_f = lane;
   asm volatile("" : "+v"(lane_f));
