@@ -499,23 +499,6 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   QBlock<1> B;
   A.q0 = q0;
   B.q0 = q0 + 32;
-#pragma unroll
-  for (int db = 0; db < kPD / 32; ++db) {
-    A.o[db] = f32x16_t{};
-    B.o[db] = f32x16_t{};
-  }
-  A.lr = f32x4_t{};
-  B.lr = f32x4_t{};
-  acc_settle(A);  // places the zeroed accumulators in AGPRs
-  acc_settle(B);
-  {
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {  // P(-1) = 0: the first body's P.V adds nothing
-      A.p[c] = __builtin_bit_cast(bf16x8_t, z);
-      B.p[c] = __builtin_bit_cast(bf16x8_t, z);
-    }
-  }
   A.mbl = B.mbl = neg_inf();
   A.g = B.g = 0.f;
   A.lim = B.lim = neg_inf();  // the first tile always rebases
@@ -807,7 +790,9 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
       // (opaque, so the compiler cannot thread the fast and the slow path
       // into two copies of the whole body)
       asm volatile("" : "+s"(rescale));
-      if (rescale) {
+      // (in the first body the accumulators are still zero: its P.V products
+      // ran on P(-1) = 0, so the rebase every row takes there moves nothing)
+      if (rescale && key0 != 0) {
         // the body's P.V products added weights of the old reference; the
         // accumulators move to the new one now
         const int src = lr_partner(lane);
@@ -850,6 +835,25 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   }
   dma_tile(0);
   dma_tile(1);
+  // the accumulators and P(-1) are zeroed while the loads fly (before them,
+  // the 136 AGPR writes would hold the first load back)
+#pragma unroll
+  for (int db = 0; db < kPD / 32; ++db) {
+    A.o[db] = f32x16_t{};
+    B.o[db] = f32x16_t{};
+  }
+  A.lr = f32x4_t{};
+  B.lr = f32x4_t{};
+  acc_settle(A);  // places the zeroed accumulators in AGPRs
+  acc_settle(B);
+  {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // P(-1) = 0: the first body's P.V adds nothing
+      A.p[c] = __builtin_bit_cast(bf16x8_t, z);
+      B.p[c] = __builtin_bit_cast(bf16x8_t, z);
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt 12: the query rows and tile 0's K landed
   wg_barrier();
   {
