@@ -57,11 +57,14 @@
 //
 // LDS: a 4-stage ring of K/V tiles, row-major with XOR-swizzled 16-byte
 // chunks, filled by direct global->LDS buffer loads (each wave moves a quarter
-// of a tile).  After the barrier that opens iteration t, the K tile t+1 and
-// the V tiles up to t have landed and tile t-2's stage is free; the loads of
-// tile t+2 go out early in the body, K before V.  The workgroup's query rows
-// come in the same way, through stages 2 and 3 before the ring first uses
-// them, and are read from there into the Q^T AGPRs.
+// of a tile); the four K tiles fill the lower 64 KB and the four V tiles the
+// upper.  After the barrier that opens iteration t, the K tile t+1 and the V
+// tiles up to t have landed and tile t-2's stage is free; the loads of tile
+// t+2 go out early in the body, K before V.  The loop runs four bodies per
+// trip, so each body's stages are compile-time constants that ride in the
+// immediate offsets of its operand reads.  The workgroup's query rows come in
+// the same way, through stages 2 and 3 before the ring first uses them, and
+// are read from there into the Q^T AGPRs.
 //
 // Masking: keys past the sequence end and (causal) keys after the query score
 // -inf ("Mini FlashAttention", section 1); a -inf reference is replaced by 0
@@ -90,6 +93,10 @@ constexpr int kPD = 128;
 constexpr int kPBN = 64;
 using PT = Bf16Tile<kPD, kPBN>;
 constexpr int kPLds = kPStages * PT::STAGE;         // 128 KB
+// LDS: the K tile of stage s at s TILE, the V tile at kPVBase + s TILE, so
+// that any operand of a stage known at compile time sits within the 16-bit
+// offset of a ds_read from a fixed per-lane address
+constexpr int kPVBase = kPStages * PT::TILE;
 constexpr int kPDpw = PT::TILE / (1024 * kPWaves);  // staging loads per wave per tensor: 4
 constexpr float kPMargin = 48.f;     // a new reference sits this far above the row max (log2)
 constexpr float kPBoundLog2 = 32.f;  // the fast path keeps every weight <= 2^32
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
         const_cast<uint16_t *>(src), (short)0,
         valid > 0 ? (int)((valid - 1) * rsb + PT::ROWB) : 0, 0x00020000);
     const int j = i >> 1;
-    char *st = smem + (st_t & (kPStages - 1)) * PT::STAGE + ((i & 1) ? PT::TILE : 0) +
+    char *st = smem + (st_t & (kPStages - 1)) * PT::TILE + ((i & 1) ? kPVBase : 0) +
                (w * kPDpw + j) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void *)st, 16,
                                              (i & 1) ? o_v[j] : o_k[j], 0, 0, 0);
@@ -578,7 +585,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>((i & 1) ? d.v : d.k), (short)0, d.rec, 0x00020000);
     const int j = i >> 1;
-    char *st = smem + (d.t & (kPStages - 1)) * PT::STAGE + ((i & 1) ? PT::TILE : 0) +
+    char *st = smem + (d.t & (kPStages - 1)) * PT::TILE + ((i & 1) ? kPVBase : 0) +
                (w * kPDpw + j) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FA_LDS void *)st, 16,
                                              (i & 1) ? o_v[j] : o_k[j], 0, 0, 0);
@@ -589,11 +596,14 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   };
 
   // ---- LDS operand addresses (byte offsets within a stage) ----------------
+  const uint32_t lds_base =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS char *)smem));
+  // LDS addresses of this lane's operands in stage 0 (a stage s adds s TILE)
   uint32_t kofs[kPD / 16];  // K operand (kb, c): row 32 kb + l32, logical chunk 2c + h
   {
     const int sw = PT::swz_k(l32);
 #pragma unroll
-    for (int c = 0; c < kPD / 16; ++c) kofs[c] = l32 * PT::ROWB + 16 * ((2 * c + h) ^ sw);
+    for (int c = 0; c < kPD / 16; ++c) kofs[c] = lds_base + l32 * PT::ROWB + 16 * ((2 * c + h) ^ sw);
   }
   uint32_t vofs[kPD / 32];  // V^T operand (db, c): key row 16c (+8) + 4h + e4, d 32db + ...
   {
@@ -601,12 +611,10 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
     const int sw = PT::swz_v(e4);
 #pragma unroll
     for (int db = 0; db < kPD / 32; ++db)
-      vofs[db] = PT::TILE + (4 * h + e4) * PT::ROWB +
+      vofs[db] = lds_base + kPVBase + (4 * h + e4) * PT::ROWB +
                  16 * ((4 * db + 2 * gq + ((j & 3) >> 1)) ^ sw) + 8 * (j & 1);
   }
-  const uint32_t lds_base =
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FA_LDS char *)smem));
-  auto stage_addr = [&](int t) { return lds_base + (t & (kPStages - 1)) * PT::STAGE; };
+  auto stage_off = [&](int t) { return static_cast<uint32_t>((t & (kPStages - 1)) * PT::TILE); };
 
   const float sl2 = a.scale_log2;
   const float inv_sl2 = 1.f / sl2;
@@ -662,10 +670,14 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   // PV: O += P V over the V tile at vbase; S: S = K Q^T over the K tile at
   // kbase; SM: the softmax of the scores of the tile at key0 (a full body
   // has all three and sends this wave's share of tile dma_t + 2).
-  auto body = [&](auto pv_c, auto s_c, auto sm_c, auto sb_c, int key0, uint32_t vbase,
-                  uint32_t kbase, const DmaTile &dn) {
+  auto body = [&](auto pv_c, auto s_c, auto sm_c, auto sb_c, auto vs_c, auto ks_c, int key0,
+                  uint32_t vbase, uint32_t kbase, const DmaTile &dn) {
     constexpr bool PV = decltype(pv_c)::value, S = decltype(s_c)::value,
                    SM = decltype(sm_c)::value;
+    // the stages of the V and the K tile when known at compile time (their
+    // offsets then ride in the ds_read immediates), else -1 and the stage
+    // offsets vbase / kbase
+    constexpr int VS = decltype(vs_c)::value, KS = decltype(ks_c)::value;
     constexpr int SB = decltype(sb_c)::value;  // S(t) in set SB, S(t+1) goes to set 1 - SB
     constexpr BodySchedule<PV, S> BS{};
     constexpr BodyWaits<PV, S> BW{};
@@ -697,10 +709,18 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
       if constexpr (k < N) {
         constexpr Slot sl = BS.slot[k];
         if constexpr (sl.kind == 0 && sl.reads > 0) {
-          lds_read_v<sl.op % NRV, 16 * sl.c * PT::ROWB, (16 * sl.c + 8) * PT::ROWB>(
-              vr[sl.op % NRV], vbase + vofs[sl.x]);
+          if constexpr (VS >= 0)
+            lds_read_v<sl.op % NRV, VS * PT::TILE + 16 * sl.c * PT::ROWB,
+                       VS * PT::TILE + (16 * sl.c + 8) * PT::ROWB>(vr[sl.op % NRV], vofs[sl.x]);
+          else
+            lds_read_v<sl.op % NRV, 16 * sl.c * PT::ROWB, (16 * sl.c + 8) * PT::ROWB>(
+                vr[sl.op % NRV], vbase + vofs[sl.x]);
         } else if constexpr (sl.kind == 2 && sl.reads > 0) {
-          lds_read_k<sl.op % NRK, sl.x * 32 * PT::ROWB>(kr[sl.op % NRK], kbase + kofs[sl.c]);
+          if constexpr (KS >= 0)
+            lds_read_k<sl.op % NRK, KS * PT::TILE + sl.x * 32 * PT::ROWB>(kr[sl.op % NRK],
+                                                                        kofs[sl.c]);
+          else
+            lds_read_k<sl.op % NRK, sl.x * 32 * PT::ROWB>(kr[sl.op % NRK], kbase + kofs[sl.c]);
         }
       }
     };
@@ -815,6 +835,9 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   using T_ = std::true_type;
   using F_ = std::false_type;
 
+  // where query piece j waits: the K tiles of stages 2 and 3, then their V
+  // tiles (none is written before the first body's barrier)
+  auto q_piece = [](int j) { return j < 2 ? (2 + j) * PT::TILE : kPVBase + j * PT::TILE; };
   // prologue: the query rows staged through stages 2 and 3 (piece j, rows
   // m0 + 64 j .. + 63, laid out as a K tile; wave w moves a quarter of each
   // piece with the K tile's offsets), tiles 0 and 1 requested; once the query
@@ -830,7 +853,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
 #pragma unroll
     for (int i = 0; i < kPDpw; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (FA_LDS void *)(smem + 2 * PT::STAGE + j * PT::TILE + (w * kPDpw + i) * 1024), 16,
+          rsrc, (FA_LDS void *)(smem + q_piece(j) + (w * kPDpw + i) * 1024), 16,
           o_k[i], 0, 0, 0);
   }
   dma_tile(0);
@@ -858,7 +881,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   wg_barrier();
   {
     // wave w's rows are piece w: block a its rows 0 .. 31, block b 32 .. 63
-    const uint32_t qa = lds_base + 2 * PT::STAGE + w * PT::TILE;
+    const uint32_t qa = q_piece(w);
     q_read<0>(A, qa, kofs);
     q_read<1>(B, qa + 32 * PT::ROWB, kofs);
   }
@@ -868,26 +891,41 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     DmaTile dn = dma_state(2);  // the loads of body t fetch tile t + 2
-    body(F_{}, T_{}, F_{}, S1{}, 0, 0u, stage_addr(0), dn);  // S(0), into set 0
-    // The first body's P.V runs on P = 0 over tile 0's V (finite data).  On
-    // the wave's last tile the score products read a stage whose contents
-    // are not used (zeros past the workgroup's last tile), which keeps the
-    // loop a straight pair of bodies.  Even tiles keep their scores in set
-    // 0, odd tiles in set 1, so a body never overwrites the scores it is
-    // still turning into weights.
+    using Vr = std::integral_constant<int, -1>;  // stage known only at run time
+    using St0 = std::integral_constant<int, 0>;
+    using St1 = std::integral_constant<int, 1>;
+    using St2 = std::integral_constant<int, 2>;
+    using St3 = std::integral_constant<int, 3>;
+    body(F_{}, T_{}, F_{}, S1{}, Vr{}, St0{}, 0, 0u, 0u, dn);  // S(0), into set 0
+    // Body t reads V from stage (t - 1) % 4 and K from stage (t + 1) % 4: the
+    // loop runs four bodies per trip, so both are compile-time constants.  The
+    // first body's P.V runs on P = 0 over stage 3, which holds query rows
+    // then (finite data).  On the wave's last tile the score products read a
+    // stage whose contents are not used (zeros past the workgroup's last
+    // tile), which keeps the loop a straight run of bodies.  Even tiles keep
+    // their scores in set 0, odd tiles in set 1, so a body never overwrites
+    // the scores it is still turning into weights.
     for (int t = 0;;) {
       open_iter();
-      body(T_{}, T_{}, T_{}, S0{}, t * kPBN, stage_addr(t > 0 ? t - 1 : 0), stage_addr(t + 1), dn);
+      body(T_{}, T_{}, T_{}, S0{}, St3{}, St1{}, t * kPBN, 0u, 0u, dn);
       dma_advance(dn);
       if (++t >= Tw) break;
       open_iter();
-      body(T_{}, T_{}, T_{}, S1{}, t * kPBN, stage_addr(t - 1), stage_addr(t + 1), dn);
+      body(T_{}, T_{}, T_{}, S1{}, St0{}, St2{}, t * kPBN, 0u, 0u, dn);
+      dma_advance(dn);
+      if (++t >= Tw) break;
+      open_iter();
+      body(T_{}, T_{}, T_{}, S0{}, St1{}, St3{}, t * kPBN, 0u, 0u, dn);
+      dma_advance(dn);
+      if (++t >= Tw) break;
+      open_iter();
+      body(T_{}, T_{}, T_{}, S1{}, St2{}, St0{}, t * kPBN, 0u, 0u, dn);
       dma_advance(dn);
       if (++t >= Tw) break;
     }
     // O += P V of the wave's last tile (its stage is not refilled before this
     // wave's next barrier)
-    body(T_{}, F_{}, F_{}, S0{}, 0, stage_addr(Tw - 1), 0u, dn);
+    body(T_{}, F_{}, F_{}, S0{}, Vr{}, Vr{}, 0, stage_off(Tw - 1), 0u, dn);
   }
   for (int t = Tw; t < T; ++t) {  // rows done: barriers and staging only
     open_iter();
