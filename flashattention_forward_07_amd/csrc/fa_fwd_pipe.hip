@@ -294,10 +294,11 @@ __device__ __forceinline__ void acc_scale(QB &x, float alpha, float alpha_lr) {
   for (int db = 0; db < kPD / 32; ++db) x.o[db] *= alpha;
   x.lr *= alpha_lr;
 }
-// Maximum of eight and of four values, each chain in one statement: the
-// compiler puts a wait state after every inline vector instruction whose
-// result the next one reads, and fmaxf on values it cannot prove canonical
-// (these come from inline products) adds canonicalising maxima.
+// Maximum of eight values, and a running maximum carried on over eight
+// more, each chain in one statement: the compiler puts a wait state after
+// every inline vector instruction whose result the next one reads, and fmaxf
+// on values it cannot prove canonical (these come from inline products) adds
+// canonicalising maxima.
 __device__ __forceinline__ float max8(float a, float b, float c, float d, float e, float f,
                                       float g, float h) {
   float r;
@@ -307,10 +308,14 @@ __device__ __forceinline__ float max8(float a, float b, float c, float d, float 
       : "v"(a), "v"(b), "v"(c), "v"(d), "v"(e), "v"(f), "v"(g), "v"(h));
   return r;
 }
-__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+// The running maximum m carried on over eight more values: four v_max3.
+__device__ __forceinline__ float max_on8(float m, float a, float b, float c, float d, float e,
+                                         float f, float g, float h) {
   float r;
-  asm volatile("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4" : "=&v"(r)
-      : "v"(a), "v"(b), "v"(c), "v"(d));
+  asm volatile("v_max3_f32 %0, %1, %2, %3\n\tv_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\tv_max3_f32 %0, %0, %8, %9"
+      : "=&v"(r)
+      : "v"(m), "v"(a), "v"(b), "v"(c), "v"(d), "v"(e), "v"(f), "v"(g), "v"(h));
   return r;
 }
 
@@ -688,7 +693,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
     static_assert(NRV <= 4 && NRK <= 4, "ring entries");
     u32x4_t vr[NRV];  // V^T operand 4c + db in entry (4c + db) % NRV
     u32x4_t kr[NRK];  // K operand 8kb + c in entry (8kb + c) % NRK
-    float mq[2][4];      // partial maxima (block, quarter)
+    float mq[2];         // running maxima of the raw scores (block)
     float ps[2][4];      // partial fp32 sums of the weights
     int rescale = 0;  // the rebase ran (kept opaque below: see the end of the body)
 
@@ -762,12 +767,17 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
           auto &x = pick<bi>(A, B);
           constexpr int r0 = 8 * j;
           const f32x16_t &sv = x.s[SB][kb];
-          mq[bi][2 * kb + j] = max8(sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
-                                    sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]);
+          // a block's four eighths run as one chain (its slots are 2 bi, 2 bi + 1,
+          // 2 bi + 4 and 2 bi + 5)
+          if constexpr (kb == 0 && j == 0)
+            mq[bi] = max8(sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4], sv[r0 + 5],
+                          sv[r0 + 6], sv[r0 + 7]);
+          else
+            mq[bi] = max_on8(mq[bi], sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3], sv[r0 + 4],
+                             sv[r0 + 5], sv[r0 + 6], sv[r0 + 7]);
         }
         if constexpr (k == kSmTest) {
-          const float ma = max4(mq[0][0], mq[0][1], mq[0][2], mq[0][3]);
-          const float mb = max4(mq[1][0], mq[1][1], mq[1][2], mq[1][3]);
+          const float ma = mq[0], mb = mq[1];
           if (__builtin_amdgcn_ballot_w64(ma > A.lim || mb > B.lim) != 0) {
             rebase(A, ma);
             rebase(B, mb);
