@@ -850,8 +850,8 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
   auto q_piece = [](int j) { return j < 2 ? (2 + j) * PT::TILE : kPVBase + j * PT::TILE; };
   // prologue: the query rows staged through stages 2 and 3 (piece j, rows
   // m0 + 64 j .. + 63, laid out as a K tile; wave w moves a quarter of each
-  // piece with the K tile's offsets), tiles 0 and 1 requested; once the query
-  // rows and tile 0's K are in LDS, Q^T goes to its AGPRs and S(0) runs
+  // piece with the K tile's offsets), then tiles 0 and 1; once the query rows
+  // and tile 0's K are in LDS, Q^T goes to its AGPRs and S(0) runs
 #pragma unroll
   for (int j = 0; j < kPBlockM / kPBN; ++j) {
     const int r0 = m0 + j * kPBN;
@@ -866,8 +866,16 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
           rsrc, (FA_LDS void *)(smem + q_piece(j) + (w * kPDpw + i) * 1024), 16,
           o_k[i], 0, 0, 0);
   }
-  dma_tile(0);
-  dma_tile(1);
+  // tiles 0 and 1, both K tiles first: S(0) waits for K(0) and the first
+  // body for K(1), while V(0) is first read in the second body
+#pragma unroll
+  for (int p = 0; p < kPDpw; ++p) dma_part(0, 0, 2 * p);
+#pragma unroll
+  for (int p = 0; p < kPDpw; ++p) dma_part(1, 1, 2 * p);
+#pragma unroll
+  for (int p = 0; p < kPDpw; ++p) dma_part(0, 0, 2 * p + 1);
+#pragma unroll
+  for (int p = 0; p < kPDpw; ++p) dma_part(1, 1, 2 * p + 1);
   // the accumulators and P(-1) are zeroed while the loads fly (before them,
   // the 136 AGPR writes would hold the first load back)
 #pragma unroll
@@ -915,8 +923,10 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
     // tile), which keeps the loop a straight run of bodies.  Even tiles keep
     // their scores in set 0, odd tiles in set 1, so a body never overwrites
     // the scores it is still turning into weights.
+    // the first body's barrier: K(1) has landed, V(0) and V(1) may still fly
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt 8
+    wg_barrier();
     for (int t = 0;;) {
-      open_iter();
       body(T_{}, T_{}, T_{}, S0{}, St3{}, St1{}, t * kPBN, 0u, 0u, dn);
       dma_advance(dn);
       if (++t >= Tw) break;
@@ -932,6 +942,7 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
       body(T_{}, T_{}, T_{}, S1{}, St2{}, St0{}, t * kPBN, 0u, 0u, dn);
       dma_advance(dn);
       if (++t >= Tw) break;
+      open_iter();
     }
     // O += P V of the wave's last tile (its stage is not refilled before this
     // wave's next barrier)
