@@ -825,9 +825,13 @@ __global__ __launch_bounds__(kPThreads, 1) void fa_fwd_bf16_pipe(const FwdArgs a
       if (rescale && key0 != 0) {
         // the body's P.V products added weights of the old reference; the
         // accumulators move to the new one now
+        // (a block none of whose rows moved its reference has alpha = 1 in
+        // every lane and is left alone)
         const int src = lr_partner(lane);
-        acc_scale(A, A.alpha, lane_fetch(A.alpha, src));
-        acc_scale(B, B.alpha, lane_fetch(B.alpha, src));
+        if (__builtin_amdgcn_ballot_w64(A.alpha != 1.f) != 0)
+          acc_scale(A, A.alpha, lane_fetch(A.alpha, src));
+        if (__builtin_amdgcn_ballot_w64(B.alpha != 1.f) != 0)
+          acc_scale(B, B.alpha, lane_fetch(B.alpha, src));
       }
     }
   };
