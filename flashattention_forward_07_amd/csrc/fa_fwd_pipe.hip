@@ -32,12 +32,16 @@
 //
 // Lazy rescaling, decided before any weight is formed: the lane's max of the
 // raw scores is compared with the largest score the current reference lets
-// through with every weight <= 2^32.  Only when some lane is over does the
+// through with every weight <= 2^64.  Only when some lane is over does the
 // wave rebase (row maxima, a reference 48 above them in the exp2 domain, l
 // scaled at once, O and the row sums scaled after the body's P.V products,
 // which still add weights of the old reference).  The weights are then formed
 // once, against the final reference.  The first tile always rebases (there
 // is no reference yet).  In exact arithmetic the reference cancels in O / l.
+// The bound leaves fp32 room: at most 2^31 weights of at most 2^64 sum below
+// 2^95, and O stays finite while every |v| is below 2^33; a wider bound
+// means fewer rebases where the scores spread over many log2 units (a bound
+// of 2^32 ran packed Q, K x 8 inputs 4 % slower).
 //
 // Registers: the two score sets and P of both blocks in VGPRs; O (2 x 64) and the
 // rounded-weight row sums (2 x 4) in AGPRs; the resident Q (2 x 32) and the
@@ -99,7 +103,7 @@ constexpr int kPLds = kPStages * PT::STAGE;         // 128 KB
 constexpr int kPVBase = kPStages * PT::TILE;
 constexpr int kPDpw = PT::TILE / (1024 * kPWaves);  // staging loads per wave per tensor: 4
 constexpr float kPMargin = 48.f;     // a new reference sits this far above the row max (log2)
-constexpr float kPBoundLog2 = 32.f;  // the fast path keeps every weight <= 2^32
+constexpr float kPBoundLog2 = 64.f;  // the fast path keeps every weight <= 2^64
 static_assert(kPDpw == 4, "staging split");
 
 // One 32-row query block of a wave (BLK 0 = a, 1 = b: which AGPRs it owns).
