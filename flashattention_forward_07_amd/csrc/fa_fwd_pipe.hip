@@ -41,7 +41,11 @@
 // The bound leaves fp32 room: at most 2^31 weights of at most 2^64 sum below
 // 2^95, and O stays finite while every |v| is below 2^33; a wider bound
 // means fewer rebases where the scores spread over many log2 units (a bound
-// of 2^32 ran packed Q, K x 8 inputs 4 % slower).
+// of 2^32 ran packed Q, K x 8 inputs 4 % slower).  Margin plus bound must
+// stay below 126: when the scores outgrow the bound, the rescale factor of
+// weights that were near the bound is 2^-(margin + bound), which has to be a
+// normal fp32 number (48 + 72 and 64 + 64 flushed it and lost those rows'
+// dominant terms).
 //
 // Registers: the two score sets and P of both blocks in VGPRs; O (2 x 64) and the
 // rounded-weight row sums (2 x 4) in AGPRs; the resident Q (2 x 32) and the
