@@ -44,7 +44,7 @@
 // of 2^32 ran packed Q, K x 8 inputs 4 % slower).  Margin plus bound must
 // stay below 126: when the scores outgrow the bound, the rescale factor of
 // weights that were near the bound is 2^-(margin + bound), which has to be a
-// normal fp32 number (48 + 72 and 64 + 64 flushed it and lost those rows'
+// normal fp32 number (48 + 80 and 64 + 64 flushed it and lost those rows'
 // dominant terms).
 //
 // Registers: the two score sets and P of both blocks in VGPRs; O (2 x 64) and the
