@@ -32,20 +32,21 @@
 //
 // Lazy rescaling, decided before any weight is formed: the lane's max of the
 // raw scores is compared with the largest score the current reference lets
-// through with every weight <= 2^64.  Only when some lane is over does the
+// through with every weight <= 2^52.  Only when some lane is over does the
 // wave rebase (row maxima, a reference 48 above them in the exp2 domain, l
 // scaled at once, O and the row sums scaled after the body's P.V products,
 // which still add weights of the old reference).  The weights are then formed
 // once, against the final reference.  The first tile always rebases (there
 // is no reference yet).  In exact arithmetic the reference cancels in O / l.
-// The bound leaves fp32 room: at most 2^31 weights of at most 2^64 sum below
-// 2^95, and O stays finite while every |v| is below 2^33; a wider bound
-// means fewer rebases where the scores spread over many log2 units (a bound
-// of 2^32 ran packed Q, K x 8 inputs 4 % slower).  Margin plus bound must
-// stay below 126: when the scores outgrow the bound, the rescale factor of
-// weights that were near the bound is 2^-(margin + bound), which has to be a
-// normal fp32 number (48 + 80 and 64 + 64 flushed it and lost those rows'
-// dominant terms).
+// The bound leaves fp32 room: at most 2^31 weights of at most 2^52 sum below
+// 2^83, and O stays finite while every |v| is below 2^45.  A wider bound
+// means fewer rebases where the scores spread over many log2 units (2^32 ran
+// packed Q, K x 8 inputs 3 % slower), but margin plus bound must stay at or
+// below 102: a rebase's factor 2^(g_old - g_new) flushes to zero once the
+// references differ by more than 126, and the old weights it then drops lie
+// below 2^(margin + bound - 126) of the new row max, which must stay under
+// 2^-24 (the fp32 rounding of the sums).  Margin 48 with bound 64 could drop
+// terms of 2^-14; 56 + 64 and 48 + 80 measurably lost dominant terms.
 //
 // Registers: the two score sets and P of both blocks in VGPRs; O (2 x 64) and the
 // rounded-weight row sums (2 x 4) in AGPRs; the resident Q (2 x 32) and the
@@ -107,7 +108,8 @@ constexpr int kPLds = kPStages * PT::STAGE;         // 128 KB
 constexpr int kPVBase = kPStages * PT::TILE;
 constexpr int kPDpw = PT::TILE / (1024 * kPWaves);  // staging loads per wave per tensor: 4
 constexpr float kPMargin = 48.f;     // a new reference sits this far above the row max (log2)
-constexpr float kPBoundLog2 = 64.f;  // the fast path keeps every weight <= 2^64
+constexpr float kPBoundLog2 = 52.f;  // the fast path keeps every weight <= 2^52
+static_assert(kPMargin + kPBoundLog2 <= 102.f, "a rebase may drop terms above 2^-24 of the row max");
 static_assert(kPDpw == 4, "staging split");
 
 // One 32-row query block of a wave (BLK 0 = a, 1 = b: which AGPRs it owns).
